@@ -1,0 +1,249 @@
+"""Benchmark of the MI355X sparse-MoE layer forward (one GPU).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-decode] [--no-cpu]
+
+One step = one moe_forward over the whole batch (router, dispatch, routed and shared SwiGLU experts,
+combine) with every input resident in HBM. The default workload is the GLM-4.5-shaped prefill layer with
+skewed expert load (N=8192, D=5120, E=160, k=8, d=1536), the prefill shape the MFMA target is quoted on;
+the GLM-5-shaped decode step (N=32 on the GLM-5 prefill weights, D=6144, E=256 in 8 groups, keep 4, k=8,
+d=2048) is measured after it and reported under "decode" with its HBM roofline.
+
+Prints one JSON line. `roofline` covers the dominant kernel (the grouped gate_up GEMM + SwiGLU), timed
+with HIP events recorded by the library on the launch stream over the timed steps; `traffic` comes from
+rocprofv3 FETCH_SIZE / WRITE_SIZE summaries under profiles/ when they were taken on the current kernel
+source. `cpu_baseline` times the oracle (routing + per-expert loop form) on the host on a bounded sample
+of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+P_BF16 = 2516.6e12  # dense bf16 MFMA, FLOP/s
+P_F32 = 157.3e12
+HBM = 8.0e12  # B/s
+METRIC = "MoE-layer tokens/s + % bf16 MFMA peak (prefill), % HBM BW (decode)"
+DOMINANT = "experts_gate_up"
+KERNEL_SOURCES = ["sparse_moe_layer_gate_amd/csrc/gemm.hip", "sparse_moe_layer_gate_amd/csrc/moe_internal.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str) -> dict | None:
+    """HBM bytes per launch of the dominant kernel from a committed rocprofv3 counter summary, if it was
+    taken on the current kernel source. Format: 'key: value' lines."""
+    path = os.path.join(ROOT, "profiles", f"{DOMINANT}_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    try:
+        return {"bytes": float(kv["hbm_bytes_per_launch"]), "fetch": float(kv["fetch_bytes_per_launch"]),
+                "write": float(kv["write_bytes_per_launch"])}
+    except KeyError:
+        return None
+
+
+def flops(w: synth.Workload, N: int) -> dict:
+    """Algorithmic work of one forward: router (fp32) and the expert GEMMs (bf16)."""
+    f32 = 2.0 * N * w.D * w.E
+    gate_up = 4.0 * w.D * (N * w.k * w.d + N * w.d_sh)  # 2 (M) (D) (2 d): routed + shared
+    down = 2.0 * w.D * (N * w.k * w.d + N * w.d_sh)
+    return {"router": f32, "gate_up": gate_up, "down": down, "bf16": gate_up + down}
+
+
+def algorithmic_bytes(w: synth.Workload, N: int, distinct: int) -> dict:
+    es = 2 if w.dtype == "bf16" else 4
+    expert = 3 * w.D * w.d * es
+    weights = distinct * expert + w.n_shared * 3 * w.D * w.d * es
+    router = 4 * w.E * w.D + 4 * w.E
+    act = es * N * w.D * 2  # x in, y out
+    gate_up = (distinct + w.n_shared) * 2 * w.d * w.D * es + es * N * w.D  # gate/up weights + x
+    return {"layer": weights + router + act, "gate_up": gate_up}
+
+
+def setup(w: synth.Workload):
+    import torch
+
+    import sparse_moe_layer_gate_amd as moe
+
+    dev = synth.experts_device(w)
+    wg, b = synth.router_host(w)
+    dev["w_router"] = torch.from_numpy(wg).cuda()
+    dev["e_bias"] = torch.from_numpy(b).cuda()
+    x = synth.x_host(w)
+    xd = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda() if x.dtype == np.uint16 else \
+        torch.from_numpy(x).cuda()
+    cfg = moe.config_of(w)
+    ws = moe.alloc_workspace(cfg, w.N)
+    y = torch.empty_like(xd)
+    counts = torch.empty(w.E, dtype=torch.int32, device="cuda")
+    weights = moe.weights_struct(cfg, dev)
+    torch.cuda.synchronize()
+    return {"cfg": cfg, "dev": dev, "weights": weights, "x": xd, "y": y, "ws": ws, "counts": counts}
+
+
+def time_forward(w: synth.Workload, st: dict, steps: int, warmup: int) -> dict:
+    import torch
+
+    import sparse_moe_layer_gate_amd as moe
+
+    def step(counts=None):
+        moe.moe_forward(st["cfg"], w.N, st["x"], st["weights"], st["y"], st["ws"], counts_out=counts)
+
+    step(st["counts"])
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    moe.profile_begin()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stages = moe.profile_end()
+    counts = st["counts"].cpu().numpy()
+    return {"ms_per_step": (t1 - t0) * 1e3 / steps, "stages": stages, "counts": counts}
+
+
+def cpu_baseline(w: synth.Workload, tokens: int) -> dict:
+    """The oracle (routing + per-expert loop form) on the first `tokens` tokens of the workload."""
+    import oracle
+
+    sub = w.with_tokens(tokens)
+    x = synth.x_host(w, 0, tokens)
+    wg, b = synth.router_host(w)
+    t0 = time.perf_counter()
+    s = oracle.scores(sub, x, wg)
+    idx, wt = oracle.select(sub, s, b)
+    t_route = time.perf_counter() - t0
+    needed = {int(e): synth.expert_host(w, int(e)) for e in np.unique(idx)}
+    table = oracle.ExpertTable(sub, needed, synth.shared_host(w))
+    t1 = time.perf_counter()
+    oracle.forward_expert_loop(sub, x, table, idx, wt)
+    t_exp = time.perf_counter() - t1
+    secs = t_route + t_exp
+    return {"value": tokens / secs, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"first {tokens} of {w.N} tokens of {w.name}: oracle routing (double logits, float32 "
+                      f"selection) + per-expert loop form in double; weight generation not timed",
+            "seconds": secs}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="glm45_prefill_skewed", choices=synth.WORKLOAD_ORDER)
+    ap.add_argument("--decode-steps", type=int, default=100)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=256)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sparse_moe_layer_gate_amd  # noqa: F401  (fails loudly if libmoe.so is missing)
+
+    w = synth.WORKLOADS[args.workload]
+    print(f"[bench] {w.name}: generating inputs", file=sys.stderr, flush=True)
+    st = setup(w)
+    r = time_forward(w, st, args.steps, args.warmup)
+    distinct = int(np.count_nonzero(r["counts"]))
+    fl = flops(w, w.N)
+    by = algorithmic_bytes(w, w.N, distinct)
+    ms = r["ms_per_step"]
+    gu_ms, gu_n = r["stages"][DOMINANT]
+    gu_avg = gu_ms / max(gu_n, 1)
+    achieved = fl["gate_up"] / (gu_avg * 1e-3)
+    traffic = read_traffic(w.name)
+    roof = {"bound": "mfma", "achieved": round(achieved / 1e12, 2), "peak": P_BF16 / 1e12, "unit": "TFLOP/s",
+            "frac": round(achieved / P_BF16, 4), "traffic": None if traffic is None else traffic["bytes"],
+            "kernel": DOMINANT, "avg_ms": round(gu_avg, 4),
+            "per_launch": f"4 D (N k d + N d_sh) = {fl['gate_up'] / 1e12:.4f} TFLOP"}
+    stage_ms = {k: round(v[0] / max(v[1], 1), 4) for k, v in r["stages"].items() if v[1]}
+    t_layer = ms * 1e-3
+    out = {
+        "metric": METRIC,
+        "value": round(w.N / t_layer, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "N": w.N, "D": w.D, "E": w.E, "n_group": w.G, "topk_group": w.TG,
+                   "k": w.k, "d_moe": w.d, "n_shared": w.n_shared, "alpha": w.alpha, "parallelism": "none"},
+        "layer": {"tflops": round((fl["bf16"] + fl["router"]) / t_layer / 1e12, 2),
+                  "mfma_frac": round(fl["bf16"] / t_layer / P_BF16, 4),
+                  "hbm_frac": round(by["layer"] / t_layer / HBM, 4),
+                  "distinct_experts": distinct, "max_rows_per_expert": int(r["counts"].max()),
+                  "stage_ms": stage_ms},
+        "roofline": roof,
+    }
+    del st
+    torch.cuda.empty_cache()
+
+    if not args.no_decode:
+        wd = synth.WORKLOADS["glm5_decode"]
+        print(f"[bench] {wd.name}: generating inputs", file=sys.stderr, flush=True)
+        sd = setup(wd)
+        rd = time_forward(wd, sd, args.decode_steps, args.warmup)
+        dd = int(np.count_nonzero(rd["counts"]))
+        byd = algorithmic_bytes(wd, wd.N, dd)
+        msd = rd["ms_per_step"]
+        gms, gn = rd["stages"][DOMINANT]
+        g_avg = gms / max(gn, 1)
+        out["decode"] = {
+            "workload": wd.name, "tokens_per_s": round(wd.N / (msd * 1e-3), 1), "ms_per_step": round(msd, 4),
+            "distinct_experts": dd,
+            "hbm_frac": round(byd["layer"] / (msd * 1e-3) / HBM, 4),
+            "algorithmic_bytes": byd["layer"],
+            "roofline": {"bound": "hbm", "achieved": round(byd["gate_up"] / (g_avg * 1e-3) / 1e9, 1),
+                         "peak": HBM / 1e9, "unit": "GB/s",
+                         "frac": round(byd["gate_up"] / (g_avg * 1e-3) / HBM, 4), "traffic": None,
+                         "kernel": DOMINANT, "avg_ms": round(g_avg, 4)},
+            "stage_ms": {k: round(v[0] / max(v[1], 1), 4) for k, v in rd["stages"].items() if v[1]},
+        }
+        del sd
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu:
+        print(f"[bench] cpu baseline: oracle on {args.cpu_tokens} tokens", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

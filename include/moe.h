@@ -1,0 +1,152 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) sparse-MoE FFN forward of GLM-4.5 / GLM-5.
+ *
+ * What the layer computes (pages as titled):
+ *  - "Group Router" (GLM-4.5), How it works: s = sigmoid(x W_g^T), a bias-free
+ *    gate evaluated in float32; s' = s + b, the correction bias used only to
+ *    choose experts; G contiguous groups scored by the sum of their two largest
+ *    s'; the topk_group best groups kept; the top-k experts by s' inside them;
+ *    weights w = alpha * s / (sum over the chosen of s + eps) from the raw s
+ *    (w = alpha * s without norm_topk_prob).
+ *  - "MoE Forward" (GLM-4.5), How it works: each routed expert is a bias-free
+ *    SwiGLU, E_i(x) = W_down (SiLU(W_gate x) * W_up x), with gate and up packed
+ *    as one (2 d, D) matrix; y_n = sum over the chosen of w E_i(x_n) + E_sh(x_n);
+ *    alpha scales only the routed sum; every token uses exactly k routed
+ *    experts plus the shared one.
+ *  - "GLM-5 . Mixture of experts" and "Shared output": the module layout (router,
+ *    routed experts, one shared MLP of width n_shared * d) and the per-expert
+ *    token lists that dispatch builds.
+ *
+ * Conventions for every call:
+ *  - Buffers: all tensor pointers are device pointers (HBM), row-major and
+ *    contiguous, 16-byte aligned, owned by the caller. The library allocates
+ *    nothing and frees nothing on these calls; scratch space is the caller's
+ *    `workspace` of at least moe_workspace_size() bytes.
+ *  - Streams: `stream` is a hipStream_t (NULL = the null stream). Every call
+ *    enqueues its kernels on it and returns without synchronising.
+ *  - Errors: configuration and argument errors are detected on the host before
+ *    anything is launched and returned as a status; a failed launch returns
+ *    MOE_ERR_HIP. No exception crosses the ABI.
+ *  - N = 0 is valid and launches nothing.
+ *  - Inputs must be finite. Router weight, bias, scores and mixture weights are
+ *    float32 whatever `dtype` says; indices are int32.
+ *  - Readings where the pages are open: discarded groups are excluded from the
+ *    top-k; ties go to the lower expert / group index (IEEE comparison, so +0
+ *    equals -0); the k slots are in (s' descending, index ascending) order, and
+ *    that order fixes the summation order of the weight denominator; alpha is
+ *    applied inside the weights, once; eps is added to the denominator as a
+ *    float32 (1e-20 rounds to 9.99999968e-21).
+ */
+#ifndef SPARSE_MOE_LAYER_GATE_AMD_MOE_H
+#define SPARSE_MOE_LAYER_GATE_AMD_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* a config field, size or pointer is invalid */
+  MOE_ERR_UNSUPPORTED = 2, /* valid per the pages, not supported by these kernels (see moe_check_config) */
+  MOE_ERR_WORKSPACE = 3,   /* workspace missing or smaller than moe_workspace_size() */
+  MOE_ERR_HIP = 4          /* a HIP launch or runtime call failed */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* The router / expert fields of the model config ("Group Router": n_group, topk_group,
+ * num_experts_per_tok, norm_topk_prob, routed_scaling_factor; "MoE Forward": moe_intermediate_size,
+ * n_shared_experts). */
+typedef struct {
+  int32_t hidden_size;           /* D: multiple of 64 */
+  int32_t n_routed_experts;      /* E: 1..512 */
+  int32_t n_group;               /* G: divides E, 1..64; E/G >= 2 when G > 1 */
+  int32_t topk_group;            /* 1..G */
+  int32_t num_experts_per_tok;   /* k: 1..32 and k <= topk_group * E / G */
+  int32_t moe_intermediate_size; /* d: multiple of 64 */
+  int32_t n_shared_experts;      /* >= 0; the shared MLP has width d * n_shared_experts */
+  float routed_scaling_factor;   /* alpha */
+  int32_t norm_topk_prob;        /* 0 or 1 */
+  float eps;                     /* added to the weight denominator (1e-20 on the pages) */
+  int32_t dtype;                 /* moe_dtype of x, the expert weights and y */
+} moe_config;
+
+/* Device pointers to the layer's weights, in the pages' canonical layouts. */
+typedef struct {
+  const float* w_router; /* [E, D] float32 */
+  const float* e_bias;   /* [E] float32 correction bias (selection only) */
+  const void* gate_up;   /* [E, 2d, D]: rows [0, d) gate, rows [d, 2d) up */
+  const void* down;      /* [E, D, d] */
+  const void* sh_gate;   /* [d_sh, D]; NULL iff n_shared_experts == 0 */
+  const void* sh_up;     /* [d_sh, D] */
+  const void* sh_down;   /* [D, d_sh] */
+} moe_weights;
+
+/* moe_route flag: read the float32 scores s [N, E] from `scores` and skip the gate GEMM. */
+#define MOE_ROUTE_SCORES_IN 1u
+
+/* Host only. MOE_OK if the config is valid and these kernels support it; otherwise
+ * MOE_ERR_INVALID_ARG (not a valid layer) or MOE_ERR_UNSUPPORTED (outside the limits above). */
+moe_status moe_check_config(const moe_config* cfg);
+
+/* Host only. Bytes of workspace moe_forward and moe_dispatch need for N tokens (0 for an invalid
+ * config). The size grows linearly in N. */
+size_t moe_workspace_size(const moe_config* cfg, int64_t N);
+
+/* Router: gate GEMM + sigmoid, then group-restricted top-k and mixture weights ("Group Router").
+ *   x        [N, D] of cfg->dtype (ignored with MOE_ROUTE_SCORES_IN)
+ *   w_router [E, D] float32 (ignored with MOE_ROUTE_SCORES_IN)
+ *   e_bias   [E] float32
+ *   scores   [N, E] float32: written with s (default) or read (MOE_ROUTE_SCORES_IN)
+ *   topk_idx [N, k] int32 out: the chosen experts in slot order
+ *   topk_w   [N, k] float32 out: their weights, alpha included
+ * Given the same float32 scores, indices and weights are bit-identical to a float32 evaluation in the
+ * order stated above (correctly rounded add, divide and multiply). */
+moe_status moe_route(const moe_config* cfg, int64_t N, const void* x, const float* w_router, const float* e_bias,
+                     float* scores, uint32_t flags, int32_t* topk_idx, float* topk_w, void* stream);
+
+/* Token-choice dispatch: per-expert token lists in the per-expert loop form of "GLM-5 . Mixture of
+ * experts", as counts, an exclusive scan and a stable placement (tokens ascending inside each expert).
+ *   topk_idx    [N, k] int32 in: expert ids in [0, E)
+ *   counts      [E] int32 out: (token, slot) pairs per expert
+ *   offsets     [E + 1] int32 out: exclusive scan of counts; offsets[E] = N * k
+ *   sorted_pair [N * k] int32 out: the flat pair index n * k + slot at each expert-sorted position
+ *   inv_row     [N * k] int32 out: the position of each pair (inverse of sorted_pair)
+ * Pairs whose id is outside [0, E) are left out of the lists (inv_row = -1); the lists are then
+ * shorter than N * k and offsets[E] says so. */
+moe_status moe_dispatch(const moe_config* cfg, int64_t N, const int32_t* topk_idx, int32_t* counts,
+                        int32_t* offsets, int32_t* sorted_pair, int32_t* inv_row, void* workspace,
+                        size_t ws_bytes, void* stream);
+
+/* The whole layer ("MoE Forward", eq. y_n): route, dispatch, the routed SwiGLU experts on bf16 MFMA
+ * (float32 accumulation; float32 arithmetic when dtype is MOE_F32), the weighted combine in a fixed
+ * order without atomics, and the unscaled shared expert.
+ *   x [N, D] and y [N, D] of cfg->dtype; y must not overlap x.
+ *   topk_idx_out [N, k], topk_w_out [N, k], counts_out [E]: optional copies of the routing (NULL to skip).
+ * Deterministic: the same inputs give bit-identical outputs. */
+moe_status moe_forward(const moe_config* cfg, int64_t N, const void* x, const moe_weights* w, void* y,
+                       int32_t* topk_idx_out, float* topk_w_out, int32_t* counts_out, void* workspace,
+                       size_t ws_bytes, void* stream);
+
+/* Static string naming a status. */
+const char* moe_status_str(moe_status status);
+
+/* Per-stage timing for measurement. moe_profile_begin() starts recording a HIP event pair, on the
+ * stream each call is given, around every kernel moe_forward / moe_route / moe_dispatch launch;
+ * moe_profile_end() waits for those events, writes the summed milliseconds and launch counts per stage
+ * (up to n_stages entries, indexed as moe_stage_name lists them) and stops recording. Returns
+ * MOE_ERR_HIP if event creation or timing fails. Not thread-safe; for measurement only. */
+moe_status moe_profile_begin(void);
+moe_status moe_profile_end(double* ms_per_stage, int32_t* launches_per_stage, int32_t n_stages);
+/* Name of stage i (NULL past the last), and the number of stages. */
+const char* moe_stage_name(int32_t stage);
+int32_t moe_stage_count(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif

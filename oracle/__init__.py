@@ -58,6 +58,8 @@ def lib():
         L.oracle_swiglu.restype = None
         L.oracle_forward_tokens.argtypes = [cp, i64, vp, vp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp]
         L.oracle_forward_expert_loop.argtypes = [cp, i64, vp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp]
+        L.oracle_num_threads.argtypes = []
+        L.oracle_num_threads.restype = ctypes.c_int
         L.oracle_param_count.argtypes = [cp, vp]
         L.oracle_param_count.restype = None
         _lib = L
@@ -246,6 +248,10 @@ def forward(w, x, wg, b, experts, shared):
     table = ExpertTable(w, experts, shared)
     y = forward_tokens(w, np.arange(x.shape[0]), x, table, idx, wt)
     return y, s, idx, wt
+
+
+def num_threads() -> int:
+    return int(lib().oracle_num_threads())
 
 
 def param_count(w) -> dict:

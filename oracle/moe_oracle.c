@@ -5,8 +5,11 @@
 #include "moe_oracle.h"
 
 #include <math.h>
+#include <omp.h>
 #include <stdlib.h>
 #include <string.h>
+
+int oracle_num_threads(void) { return omp_get_max_threads(); }
 
 static double widen(const void* p, int dt, int64_t i) {
   if (dt == ORACLE_F32) return (double)((const float*)p)[i];

@@ -104,6 +104,9 @@ int oracle_forward_expert_loop(const oracle_cfg* c, int64_t N, const void* x, in
                                const void* sh_up, const void* sh_down, int wdt, const int32_t* idx,
                                const float* w, float* y);
 
+/* Threads the oracle's parallel loops use (OpenMP's maximum). */
+int oracle_num_threads(void);
+
 /* Parameter accounting of one MoE block: out = {router (W_g + bias), one routed expert, all routed
  * experts, shared expert, total, used per token (router + k routed + shared)}. */
 void oracle_param_count(const oracle_cfg* c, int64_t out[6]);

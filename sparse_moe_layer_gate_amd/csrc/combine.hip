@@ -1,0 +1,79 @@
+// Combine ("MoE Forward", eq. y_n): y_n = sum over the k slots of the weighted expert rows (already
+// scaled by w in the down GEMM) + the shared expert's row, accumulated in float32 in slot order and
+// then the shared term, rounded once to the output type. No atomics: the same inputs always give the
+// same bits.
+#include <hip/hip_runtime.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int MAX_K = 32;
+
+__device__ inline void add8(float* acc, const uint16_t* p) {
+  const uint4 v = *(const uint4*)p;
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc[2 * i] += __uint_as_float(w[i] << 16);
+    acc[2 * i + 1] += __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ inline void add8(float* acc, const float* p) {
+  const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+  acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+  acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+}
+__device__ inline uint16_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ inline void store8(uint16_t* p, const float* acc) {
+  uint4 v;
+  v.x = (uint32_t)bf16_rne(acc[0]) | ((uint32_t)bf16_rne(acc[1]) << 16);
+  v.y = (uint32_t)bf16_rne(acc[2]) | ((uint32_t)bf16_rne(acc[3]) << 16);
+  v.z = (uint32_t)bf16_rne(acc[4]) | ((uint32_t)bf16_rne(acc[5]) << 16);
+  v.w = (uint32_t)bf16_rne(acc[6]) | ((uint32_t)bf16_rne(acc[7]) << 16);
+  *(uint4*)p = v;
+}
+__device__ inline void store8(float* p, const float* acc) {
+  *(float4*)p = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  *(float4*)(p + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+}
+
+// One block per token; each thread owns 8 consecutive features per pass.
+template <typename T>
+__global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ Y, const T* __restrict__ Ysh,
+                                                      const int32_t* __restrict__ inv_row, int k, int D,
+                                                      T* __restrict__ y) {
+  __shared__ int rows[MAX_K];
+  const int64_t n = blockIdx.x;
+  if (threadIdx.x < k) rows[threadIdx.x] = inv_row[n * k + threadIdx.x];
+  __syncthreads();
+  for (int c = threadIdx.x * 8; c < D; c += 256 * 8) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int slot = 0; slot < k; ++slot) {
+      const int r = rows[slot];
+      if (r >= 0) add8(acc, Y + (int64_t)r * D + c);
+    }
+    if (Ysh) add8(acc, Ysh + n * D + c);
+    store8(y + n * D + c, acc);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(int dtype, const void* Y, const void* Ysh, const int32_t* inv_row, int64_t N, int k, int D,
+                          void* y, hipStream_t s) {
+  if (dtype == MOE_F32)
+    hipLaunchKernelGGL(combine_kernel<float>, dim3((unsigned)N), dim3(256), 0, s, (const float*)Y, (const float*)Ysh,
+                       inv_row, k, D, (float*)y);
+  else
+    hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3((unsigned)N), dim3(256), 0, s, (const uint16_t*)Y,
+                       (const uint16_t*)Ysh, inv_row, k, D, (uint16_t*)y);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,329 @@
+// C ABI entry points (declared and documented in include/moe.h): argument checks on the host, the
+// workspace carve-up, and the launch sequence of the forward on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <vector>
+
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int kMaxE = 512, kMaxG = 64, kMaxK = 32;
+
+moe_status check_cfg(const moe_config* c) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  const int D = c->hidden_size, E = c->n_routed_experts, G = c->n_group, TG = c->topk_group;
+  const int k = c->num_experts_per_tok, d = c->moe_intermediate_size;
+  if (D < 1 || E < 1 || d < 1 || k < 1 || c->n_shared_experts < 0) return MOE_ERR_INVALID_ARG;
+  if (G < 1 || E % G != 0 || TG < 1 || TG > G) return MOE_ERR_INVALID_ARG;
+  if (G > 1 && E / G < 2) return MOE_ERR_INVALID_ARG;  // a group's score needs two members
+  if ((int64_t)k > (int64_t)TG * (E / G)) return MOE_ERR_INVALID_ARG;
+  if (c->norm_topk_prob != 0 && c->norm_topk_prob != 1) return MOE_ERR_INVALID_ARG;
+  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (!std::isfinite(c->routed_scaling_factor) || !std::isfinite(c->eps) || c->eps < 0.f) return MOE_ERR_INVALID_ARG;
+  if (E > kMaxE || G > kMaxG || k > kMaxK) return MOE_ERR_UNSUPPORTED;
+  if (D % 64 != 0 || d % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)d * c->n_shared_experts > (1 << 24)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status check_n(const moe_config* c, int64_t N) {
+  if (N < 0) return MOE_ERR_INVALID_ARG;
+  // row positions (N k routed + N shared) and token ids are int32
+  if (N * (int64_t)(c->num_experts_per_tok + 1) >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct Workspace {
+  size_t scores, idx, w, chunk_counts, chunk_base, counts, offsets, sorted_pair, inv_row, tiles0, tiles1, ntiles;
+  size_t H, Hsh, Y, Ysh, total;
+  int64_t max_tiles0, max_tiles1;
+  int bm0, bm1;
+};
+
+Workspace layout(const moe_config* c, int64_t N) {
+  Workspace w{};
+  const int64_t E = c->n_routed_experts, k = c->num_experts_per_tok, D = c->hidden_size;
+  const int64_t d = c->moe_intermediate_size, dsh = d * c->n_shared_experts;
+  const int64_t es = c->dtype == MOE_F32 ? 4 : 2;
+  const int64_t nchunks = (N + kDispatchChunk - 1) / kDispatchChunk;
+  const int shp = c->n_shared_experts > 0;
+  w.bm0 = gemm_bm(c->dtype, N, (int)k, (int)E);
+  w.bm1 = w.bm0;
+  w.max_tiles0 = max_tiles(N, (int)k, (int)E, shp, w.bm0);
+  w.max_tiles1 = max_tiles(N, (int)k, (int)E, shp, w.bm1);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  w.scores = take(sizeof(float) * N * E);
+  w.idx = take(sizeof(int32_t) * N * k);
+  w.w = take(sizeof(float) * N * k);
+  w.chunk_counts = take(sizeof(int32_t) * nchunks * E);
+  w.chunk_base = take(sizeof(int32_t) * nchunks * E);
+  w.counts = take(sizeof(int32_t) * E);
+  w.offsets = take(sizeof(int32_t) * (E + 1));
+  w.sorted_pair = take(sizeof(int32_t) * N * k);
+  w.inv_row = take(sizeof(int32_t) * N * k);
+  w.tiles0 = take(sizeof(Tile) * w.max_tiles0);
+  w.tiles1 = take(sizeof(Tile) * w.max_tiles1);
+  w.ntiles = take(sizeof(int32_t) * 2);
+  w.H = take(es * N * k * d);
+  w.Hsh = take(es * N * dsh);
+  w.Y = take(es * N * k * D);
+  w.Ysh = take(es * N * D);
+  w.total = o;
+  return w;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return (T*)((char*)ws + off);
+}
+
+// ---- per-stage timing ----
+struct ProfRec {
+  int stage;
+  hipEvent_t a, b;
+};
+bool g_prof_on = false;
+bool g_prof_err = false;
+std::vector<ProfRec> g_recs;
+std::vector<hipEvent_t> g_pool;
+size_t g_pool_next = 0;
+
+hipEvent_t next_event() {
+  if (g_pool_next == g_pool.size()) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) {
+      g_prof_err = true;
+      return nullptr;
+    }
+    g_pool.push_back(e);
+  }
+  return g_pool[g_pool_next++];
+}
+
+const char* kStageNames[ST_COUNT_STAGES] = {"router_split", "router_logits", "router_select",  "dispatch_count",
+                                            "dispatch_scan", "dispatch_place", "experts_gate_up", "experts_down",
+                                            "combine"};
+
+#define MOE_TRY(stage, expr)                 \
+  do {                                       \
+    prof_before((stage), s);                 \
+    const hipError_t e_ = (expr);            \
+    prof_after((stage), s);                  \
+    if (e_ != hipSuccess) return MOE_ERR_HIP; \
+  } while (0)
+
+moe_status route_impl(const moe_config* c, int64_t N, const void* x, const float* wg, const float* bias,
+                      float* scores, uint32_t flags, int32_t* idx, float* w, hipStream_t s) {
+  const int E = c->n_routed_experts;
+  if (!(flags & MOE_ROUTE_SCORES_IN))
+    MOE_TRY(ST_LOGITS, launch_logits(c->dtype, x, wg, nullptr, N, c->hidden_size, E, scores, s));
+  MOE_TRY(ST_SELECT, launch_select(scores, bias, N, E, c->n_group, c->topk_group, c->num_experts_per_tok,
+                                   c->routed_scaling_factor, c->norm_topk_prob, c->eps, idx, w, s));
+  return MOE_OK;
+}
+
+moe_status dispatch_impl(const moe_config* c, int64_t N, const int32_t* idx, int32_t* counts, int32_t* offsets,
+                         int32_t* sorted_pair, int32_t* inv_row, void* ws, const Workspace& L, hipStream_t s) {
+  const int E = c->n_routed_experts, k = c->num_experts_per_tok;
+  const int nchunks = (int)((N + kDispatchChunk - 1) / kDispatchChunk);
+  int32_t* ntiles = at<int32_t>(ws, L.ntiles);
+  TileSpec t0{L.bm0, at<Tile>(ws, L.tiles0), ntiles};
+  TileSpec t1{L.bm1, at<Tile>(ws, L.tiles1), ntiles + 1};
+  MOE_TRY(ST_COUNT, launch_count(idx, N, k, E, at<int32_t>(ws, L.chunk_counts), s));
+  MOE_TRY(ST_SCAN, launch_scan(at<int32_t>(ws, L.chunk_counts), nchunks, N, k, E, c->n_shared_experts > 0, counts,
+                               offsets, at<int32_t>(ws, L.chunk_base), t0, t1, s));
+  MOE_TRY(ST_PLACE, launch_place(idx, N, k, E, at<int32_t>(ws, L.chunk_base), sorted_pair, inv_row, s));
+  return MOE_OK;
+}
+
+}  // namespace
+
+namespace moe {
+
+void prof_before(int stage, hipStream_t s) {
+  if (!g_prof_on) return;
+  ProfRec r{stage, next_event(), next_event()};
+  if (!r.a || !r.b || hipEventRecord(r.a, s) != hipSuccess) {
+    g_prof_err = true;
+    return;
+  }
+  g_recs.push_back(r);
+}
+
+void prof_after(int stage, hipStream_t s) {
+  if (!g_prof_on || g_recs.empty() || g_recs.back().stage != stage) return;
+  if (hipEventRecord(g_recs.back().b, s) != hipSuccess) g_prof_err = true;
+}
+
+}  // namespace moe
+
+extern "C" {
+
+moe_status moe_check_config(const moe_config* cfg) { return check_cfg(cfg); }
+
+size_t moe_workspace_size(const moe_config* cfg, int64_t N) {
+  if (check_cfg(cfg) != MOE_OK || check_n(cfg, N) != MOE_OK) return 0;
+  return layout(cfg, N).total;
+}
+
+moe_status moe_route(const moe_config* cfg, int64_t N, const void* x, const float* w_router, const float* e_bias,
+                     float* scores, uint32_t flags, int32_t* topk_idx, float* topk_w, void* stream) {
+  moe_status st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if ((st = check_n(cfg, N)) != MOE_OK) return st;
+  if (flags & ~MOE_ROUTE_SCORES_IN) return MOE_ERR_INVALID_ARG;
+  if (N == 0) return MOE_OK;
+  if (!e_bias || !scores || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
+  if (!(flags & MOE_ROUTE_SCORES_IN) && (!x || !w_router)) return MOE_ERR_INVALID_ARG;
+  return route_impl(cfg, N, x, w_router, e_bias, scores, flags, topk_idx, topk_w, (hipStream_t)stream);
+}
+
+moe_status moe_dispatch(const moe_config* cfg, int64_t N, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
+                        int32_t* sorted_pair, int32_t* inv_row, void* workspace, size_t ws_bytes, void* stream) {
+  moe_status st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if ((st = check_n(cfg, N)) != MOE_OK) return st;
+  if (!counts || !offsets) return MOE_ERR_INVALID_ARG;
+  if (N > 0 && (!topk_idx || !sorted_pair || !inv_row)) return MOE_ERR_INVALID_ARG;
+  const Workspace L = layout(cfg, N);
+  if (!workspace || ws_bytes < L.total || !aligned16(workspace)) return MOE_ERR_WORKSPACE;
+  if (N == 0) {
+    // empty lists: zero counts and offsets
+    hipStream_t s = (hipStream_t)stream;
+    if (hipMemsetAsync(counts, 0, sizeof(int32_t) * cfg->n_routed_experts, s) != hipSuccess) return MOE_ERR_HIP;
+    if (hipMemsetAsync(offsets, 0, sizeof(int32_t) * (cfg->n_routed_experts + 1), s) != hipSuccess)
+      return MOE_ERR_HIP;
+    return MOE_OK;
+  }
+  return dispatch_impl(cfg, N, topk_idx, counts, offsets, sorted_pair, inv_row, workspace, L, (hipStream_t)stream);
+}
+
+moe_status moe_forward(const moe_config* cfg, int64_t N, const void* x, const moe_weights* wt, void* y,
+                       int32_t* topk_idx_out, float* topk_w_out, int32_t* counts_out, void* workspace, size_t ws_bytes,
+                       void* stream) {
+  moe_status st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if ((st = check_n(cfg, N)) != MOE_OK) return st;
+  if (!wt) return MOE_ERR_INVALID_ARG;
+  const bool shared = cfg->n_shared_experts > 0;
+  if (N == 0) return MOE_OK;
+  if (!x || !y || !wt->w_router || !wt->e_bias || !wt->gate_up || !wt->down) return MOE_ERR_INVALID_ARG;
+  if (shared && (!wt->sh_gate || !wt->sh_up || !wt->sh_down)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(wt->w_router) || !aligned16(wt->gate_up) || !aligned16(wt->down))
+    return MOE_ERR_INVALID_ARG;
+  if (shared && (!aligned16(wt->sh_gate) || !aligned16(wt->sh_up) || !aligned16(wt->sh_down)))
+    return MOE_ERR_INVALID_ARG;
+  if (x == y) return MOE_ERR_INVALID_ARG;
+  const Workspace L = layout(cfg, N);
+  if (!workspace || ws_bytes < L.total || !aligned16(workspace)) return MOE_ERR_WORKSPACE;
+
+  hipStream_t s = (hipStream_t)stream;
+  void* ws = workspace;
+  const int E = cfg->n_routed_experts, k = cfg->num_experts_per_tok, D = cfg->hidden_size;
+  const int d = cfg->moe_intermediate_size, dsh = d * cfg->n_shared_experts;
+  const int64_t es = cfg->dtype == MOE_F32 ? 4 : 2;
+
+  int32_t* idx = at<int32_t>(ws, L.idx);
+  float* w = at<float>(ws, L.w);
+  int32_t* counts = at<int32_t>(ws, L.counts);
+  int32_t* sorted_pair = at<int32_t>(ws, L.sorted_pair);
+  int32_t* inv_row = at<int32_t>(ws, L.inv_row);
+
+  if ((st = route_impl(cfg, N, x, wt->w_router, wt->e_bias, at<float>(ws, L.scores), 0, idx, w, s)) != MOE_OK)
+    return st;
+  if ((st = dispatch_impl(cfg, N, idx, counts, at<int32_t>(ws, L.offsets), sorted_pair, inv_row, ws, L, s)) != MOE_OK)
+    return st;
+
+  GroupedArgs g{};
+  g.sorted_pair = sorted_pair;
+  g.topk_w = w;
+  g.k = k;
+  // gate_up + SwiGLU: routed rows gather x through sorted_pair; the shared expert reads x in order
+  g.tiles = at<Tile>(ws, L.tiles0);
+  g.n_tiles = at<int32_t>(ws, L.ntiles);
+  g.prob[0] = ExpertProblem{x, D, 1, wt->gate_up, (const char*)wt->gate_up + es * (int64_t)d * D, 2LL * d * D, D, d,
+                            at<void>(ws, L.H), d, 0};
+  if (shared)
+    g.prob[1] = ExpertProblem{x, D, 0, wt->sh_gate, wt->sh_up, 0, D, dsh, at<void>(ws, L.Hsh), dsh, 0};
+  MOE_TRY(ST_GATE_UP, launch_gate_up(cfg->dtype, g, L.max_tiles0, s));
+  // down + mixture weight (routed) / weight 1 (shared)
+  g.tiles = at<Tile>(ws, L.tiles1);
+  g.n_tiles = at<int32_t>(ws, L.ntiles) + 1;
+  g.prob[0] = ExpertProblem{at<void>(ws, L.H), d, 0, wt->down, nullptr, (int64_t)D * d, d, D, at<void>(ws, L.Y), D, 1};
+  if (shared)
+    g.prob[1] = ExpertProblem{at<void>(ws, L.Hsh), dsh, 0, wt->sh_down, nullptr, 0, dsh, D, at<void>(ws, L.Ysh), D, 0};
+  MOE_TRY(ST_DOWN, launch_down(cfg->dtype, g, L.max_tiles1, s));
+  MOE_TRY(ST_COMBINE, launch_combine(cfg->dtype, at<void>(ws, L.Y), shared ? at<void>(ws, L.Ysh) : nullptr, inv_row, N,
+                                     k, D, y, s));
+
+  if (topk_idx_out && hipMemcpyAsync(topk_idx_out, idx, sizeof(int32_t) * N * k, hipMemcpyDeviceToDevice, s))
+    return MOE_ERR_HIP;
+  if (topk_w_out && hipMemcpyAsync(topk_w_out, w, sizeof(float) * N * k, hipMemcpyDeviceToDevice, s))
+    return MOE_ERR_HIP;
+  if (counts_out && hipMemcpyAsync(counts_out, counts, sizeof(int32_t) * E, hipMemcpyDeviceToDevice, s))
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+const char* moe_status_str(moe_status status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: invalid config field, size or pointer";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: valid layer outside the kernels' limits";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing, misaligned or too small";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP launch or runtime call failed";
+  }
+  return "unknown moe_status";
+}
+
+moe_status moe_profile_begin(void) {
+  g_recs.clear();
+  g_pool_next = 0;
+  g_prof_err = false;
+  g_prof_on = true;
+  return MOE_OK;
+}
+
+moe_status moe_profile_end(double* ms_per_stage, int32_t* launches_per_stage, int32_t n_stages) {
+  g_prof_on = false;
+  for (int i = 0; i < n_stages; ++i) {
+    if (ms_per_stage) ms_per_stage[i] = 0.0;
+    if (launches_per_stage) launches_per_stage[i] = 0;
+  }
+  moe_status st = g_prof_err ? MOE_ERR_HIP : MOE_OK;
+  for (const ProfRec& r : g_recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) {
+      st = MOE_ERR_HIP;
+      continue;
+    }
+    if (r.stage < n_stages) {
+      if (ms_per_stage) ms_per_stage[r.stage] += ms;
+      if (launches_per_stage) launches_per_stage[r.stage] += 1;
+    }
+  }
+  g_recs.clear();
+  g_pool_next = 0;
+  return st;
+}
+
+const char* moe_stage_name(int32_t stage) {
+  return (stage >= 0 && stage < ST_COUNT_STAGES) ? kStageNames[stage] : nullptr;
+}
+
+int32_t moe_stage_count(void) { return ST_COUNT_STAGES; }
+
+}  // extern "C"

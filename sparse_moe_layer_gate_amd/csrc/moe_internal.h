@@ -1,0 +1,91 @@
+// Internal declarations shared by the library's translation units (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+// Stages of the forward, in launch order; each has its own timing slot.
+enum Stage {
+  ST_ROUTER_SPLIT = 0,  // float32 router weight -> three bfloat16 pieces
+  ST_LOGITS,            // gate GEMM + sigmoid -> scores
+  ST_SELECT,            // bias, group stage, top-k, weights
+  ST_COUNT,             // per-chunk expert histogram
+  ST_SCAN,              // offsets, chunk bases, tile lists
+  ST_PLACE,             // stable placement -> sorted_pair / inv_row
+  ST_GATE_UP,           // grouped gate_up GEMM + SwiGLU (routed and shared)
+  ST_DOWN,              // grouped down GEMM + weight scale (routed and shared)
+  ST_COMBINE,           // y = sum of weighted rows + shared row
+  ST_COUNT_STAGES
+};
+
+// One row tile of a grouped GEMM: problem 0 = routed experts, 1 = shared expert.
+struct Tile {
+  int32_t problem;
+  int32_t expert;
+  int32_t row_start;  // first row in the problem's row space
+  int32_t rows;       // valid rows in this tile (1..BM)
+};
+
+// Profiling hooks (no-ops unless moe_profile_begin() was called).
+void prof_before(int stage, hipStream_t s);
+void prof_after(int stage, hipStream_t s);
+
+constexpr int kDispatchChunk = 256;  // tokens per dispatch block
+
+// ---- router ----
+hipError_t launch_router_split(const float* wg, int E, int D, uint16_t* wsplit, hipStream_t s);
+hipError_t launch_logits(int dtype, const void* x, const float* wg, const uint16_t* wsplit, int64_t N, int D, int E,
+                         float* scores, hipStream_t s);
+hipError_t launch_select(const float* scores, const float* bias, int64_t N, int E, int G, int TG, int k, float alpha,
+                         int norm, float eps, int32_t* idx, float* w, hipStream_t s);
+
+// ---- dispatch ----
+struct TileSpec {
+  int bm;            // rows per tile
+  Tile* tiles;       // output list
+  int32_t* n_tiles;  // output count
+};
+hipError_t launch_count(const int32_t* idx, int64_t N, int k, int E, int32_t* chunk_counts, hipStream_t s);
+hipError_t launch_scan(const int32_t* chunk_counts, int nchunks, int64_t N, int k, int E, int n_shared_problem,
+                       int32_t* counts, int32_t* offsets, int32_t* chunk_base, TileSpec t0, TileSpec t1,
+                       hipStream_t s);
+hipError_t launch_place(const int32_t* idx, int64_t N, int k, int E, const int32_t* chunk_base, int32_t* sorted_pair,
+                        int32_t* inv_row, hipStream_t s);
+
+// ---- grouped expert GEMMs ----
+struct ExpertProblem {
+  const void* A;       // activation rows
+  int64_t lda;         // elements between rows of A
+  int gather;          // 1: A row = sorted_pair[row] / k (rows of x in expert order); 0: A row = row
+  const void* B0;      // gate rows (gate_up) or down rows, expert 0
+  const void* B1;      // up rows (gate_up), expert 0
+  int64_t b_stride;    // elements between consecutive experts' B
+  int K;               // reduction length
+  int ncols;           // output columns
+  void* out;           // [rows, ncols]
+  int64_t ldo;
+  int scale_rows;      // 1: multiply row r by topk_w[sorted_pair[r]]
+};
+struct GroupedArgs {
+  ExpertProblem prob[2];
+  const Tile* tiles;
+  const int32_t* n_tiles;
+  const int32_t* sorted_pair;
+  const float* topk_w;
+  int k;
+};
+// Upper bound on tiles for a tile list with bm rows per tile.
+int64_t max_tiles(int64_t N, int k, int E, int n_shared_problem, int bm);
+int gemm_bm(int dtype, int64_t N, int k, int E);  // rows per tile the forward will use
+hipError_t launch_gate_up(int dtype, const GroupedArgs& a, int64_t max_tile_count, hipStream_t s);
+hipError_t launch_down(int dtype, const GroupedArgs& a, int64_t max_tile_count, hipStream_t s);
+
+// ---- combine ----
+hipError_t launch_combine(int dtype, const void* Y, const void* Ysh, const int32_t* inv_row, int64_t N, int k, int D,
+                          void* y, hipStream_t s);
+
+}  // namespace moe

@@ -183,8 +183,10 @@ def expert_host(w: Workload, e: int) -> tuple[np.ndarray, np.ndarray]:
     return gu, dn
 
 
-def shared_host(w: Workload) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
-    """Shared expert: (gate [d_sh, D], up [d_sh, D], down [D, d_sh]) in the workload dtype."""
+def shared_host(w: Workload):
+    """Shared expert: (gate [d_sh, D], up [d_sh, D], down [D, d_sh]) in the workload dtype; None without one."""
+    if w.n_shared == 0:
+        return None
     n = w.d_sh * w.D
     g = normal(w.seed, ID_SH_GATE, 0, n, 1.0 / math.sqrt(w.D), w.dtype).reshape(w.d_sh, w.D)
     u = normal(w.seed, ID_SH_UP, 0, n, 1.0 / math.sqrt(w.D), w.dtype).reshape(w.d_sh, w.D)
@@ -226,13 +228,14 @@ def experts_device(w: Workload, device="cuda") -> dict:
     out = {
         "gate_up": torch.empty((w.E, 2 * w.d, w.D), dtype=dt, device=device),
         "down": torch.empty((w.E, w.D, w.d), dtype=dt, device=device),
-        "sh_gate": torch.empty((w.d_sh, w.D), dtype=dt, device=device),
-        "sh_up": torch.empty((w.d_sh, w.D), dtype=dt, device=device),
-        "sh_down": torch.empty((w.D, w.d_sh), dtype=dt, device=device),
     }
     _dev_fill(out["gate_up"], w.seed, ID_GATE_UP, 0, 1.0 / math.sqrt(w.D))
     _dev_fill(out["down"], w.seed, ID_DOWN, 0, 1.0 / math.sqrt(w.d))
-    _dev_fill(out["sh_gate"], w.seed, ID_SH_GATE, 0, 1.0 / math.sqrt(w.D))
-    _dev_fill(out["sh_up"], w.seed, ID_SH_UP, 0, 1.0 / math.sqrt(w.D))
-    _dev_fill(out["sh_down"], w.seed, ID_SH_DOWN, 0, 1.0 / math.sqrt(w.d_sh))
+    if w.n_shared > 0:
+        out["sh_gate"] = torch.empty((w.d_sh, w.D), dtype=dt, device=device)
+        out["sh_up"] = torch.empty((w.d_sh, w.D), dtype=dt, device=device)
+        out["sh_down"] = torch.empty((w.D, w.d_sh), dtype=dt, device=device)
+        _dev_fill(out["sh_gate"], w.seed, ID_SH_GATE, 0, 1.0 / math.sqrt(w.D))
+        _dev_fill(out["sh_up"], w.seed, ID_SH_UP, 0, 1.0 / math.sqrt(w.D))
+        _dev_fill(out["sh_down"], w.seed, ID_SH_DOWN, 0, 1.0 / math.sqrt(w.d_sh))
     return out

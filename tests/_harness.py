@@ -1,0 +1,137 @@
+"""Shared GPU test plumbing: seeded inputs on host and device, calls through the C ABI, oracle references.
+
+Inputs come only from synth (the seeded generator); expected values come only from oracle. Nothing
+here computes any step of the layer itself.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+import oracle
+import synth
+
+
+def torch_mod():
+    import torch
+
+    return torch
+
+
+def to_device(a: np.ndarray, device="cuda"):
+    """Host array (float32, int32, or bf16 bits as uint16) -> device tensor of the matching dtype."""
+    torch = torch_mod()
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def to_host(t) -> np.ndarray:
+    torch = torch_mod()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def as_f32(a: np.ndarray) -> np.ndarray:
+    return synth.bf16_to_f32(a) if a.dtype == np.uint16 else a.astype(np.float32)
+
+
+_weight_cache = {}
+
+
+def device_weights(w: synth.Workload, generate_on_device: bool):
+    """Router (host + device) and expert weights (device) of workload w; the expert weights are cached per
+    weight recipe so that workloads sharing weights (prefill / decode) generate them once."""
+    torch = torch_mod()
+    key = (w.seed, w.D, w.E, w.d, w.n_shared, w.dtype, w.skew)
+    if key not in _weight_cache:
+        _weight_cache.clear()
+        torch.cuda.empty_cache()
+        wg, b = synth.router_host(w)
+        if generate_on_device:
+            dev = synth.experts_device(w)
+        else:
+            gu, dn = synth.all_experts_host(w)
+            dev = {"gate_up": to_device(gu), "down": to_device(dn)}
+            sh = synth.shared_host(w)
+            if sh is not None:
+                dev.update(sh_gate=to_device(sh[0]), sh_up=to_device(sh[1]), sh_down=to_device(sh[2]))
+        dev["w_router"] = to_device(wg)
+        dev["e_bias"] = to_device(b)
+        torch.cuda.synchronize()
+        _weight_cache[key] = (wg, b, dev)
+    return _weight_cache[key]
+
+
+def drop_weights():
+    torch = torch_mod()
+    _weight_cache.clear()
+    torch.cuda.empty_cache()
+
+
+def expert_table(w: synth.Workload, experts) -> oracle.ExpertTable:
+    """Host copies of the listed experts (regenerated from the seeded streams) and the shared expert."""
+    needed = {int(e): synth.expert_host(w, int(e)) for e in sorted(set(int(e) for e in experts))}
+    return oracle.ExpertTable(w, needed, synth.shared_host(w))
+
+
+def gpu_forward(w: synth.Workload, x_dev, dev_w: dict):
+    """moe_forward through the C ABI; returns (y, idx, wt, counts) as host arrays."""
+    import sparse_moe_layer_gate_amd as moe
+
+    torch = torch_mod()
+    cfg = moe.config_of(w)
+    N = x_dev.shape[0]
+    ws = moe.alloc_workspace(cfg, N)
+    y = torch.empty_like(x_dev)
+    idx = torch.empty((N, w.k), dtype=torch.int32, device="cuda")
+    wt = torch.empty((N, w.k), dtype=torch.float32, device="cuda")
+    counts = torch.empty((w.E,), dtype=torch.int32, device="cuda")
+    moe.moe_forward(cfg, N, x_dev, dev_w, y, ws, idx, wt, counts)
+    torch.cuda.synchronize()
+    out = to_host(y), to_host(idx), to_host(wt), to_host(counts)
+    del ws, y
+    return out
+
+
+def score_tolerance(w: synth.Workload, x: np.ndarray, wg: np.ndarray) -> np.ndarray:
+    """Per-element bound on |s_gpu - s_oracle|, from float32 accumulation of D exact products:
+    |dr| <= D u sum_t |x_t W_t| + ulp(r) (u = 2^-24); sigmoid has slope <= 1/4; plus 4 ulp of [0, 1] for
+    the device exp and divide."""
+    xa = np.abs(as_f32(x)).astype(np.float64)
+    wa = np.abs(wg).astype(np.float64)
+    absdot = xa @ wa.T
+    u = 2.0 ** -24
+    return 0.25 * (w.D * u * absdot + absdot * u) + 4 * u
+
+
+def sample_tokens(N: int, count: int, seed: int = 0) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    fixed = [0, N - 1, N // 2]
+    extra = rng.choice(N, size=min(count, N), replace=False)
+    return np.unique(np.concatenate([np.array(fixed[: min(3, N)]), extra]))[:max(count, 1) + 3]
+
+
+def rel_err(y: np.ndarray, ref: np.ndarray) -> float:
+    ref64 = ref.astype(np.float64)
+    den = np.abs(ref64).max()
+    return float(np.abs(y.astype(np.float64) - ref64).max() / (den if den > 0 else 1.0))
+
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def bf16_bits(a: np.ndarray) -> np.ndarray:
+    return synth.f32_to_bf16(a)
+
+
+def isclose_ulps(a, b, n):
+    a = np.asarray(a, np.float32)
+    b = np.asarray(b, np.float32)
+    return np.abs(a.astype(np.float64) - b) <= n * np.spacing(np.maximum(np.abs(a), np.abs(b)))
+
+
+def std_of(fan_in):
+    return 1.0 / math.sqrt(fan_in)

@@ -1,0 +1,114 @@
+"""GPU parity of the whole layer (moe_forward through the C ABI) against the oracle.
+
+Protocol: the GPU's expert ids must equal the oracle's for every token whose oracle decision gap exceeds
+the score error bound (near-ties may flip); the output is compared per token with the oracle evaluated
+on the oracle's routing, or on the GPU's routing for the near-tie tokens, at max|dy| / max|y| <= 1e-4
+(float32 layers) or <= 2e-2 (bfloat16 layers). Full-size workloads are checked on sampled tokens (every
+token's routing is checked); small shapes that span several tiles and ragged tails are checked whole.
+"""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import _harness as H
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_forward(w, x, wg, b, y, idx, wt, counts, tokens, on_device_weights):
+    """Routing check over all tokens, output check over `tokens`."""
+    s_ref = oracle.scores(w, x, wg)
+    idx_ref, w_ref = oracle.select(w, s_ref, b)
+    margin = oracle.select_margin(w, s_ref, b)
+    tol_s = H.score_tolerance(w, x, wg).max(axis=1)
+    differ = np.any(idx != idx_ref, axis=1)
+    assert np.all(margin[differ] <= 2 * tol_s[differ]), "a routing difference away from a near-tie"
+    assert np.array_equal(counts, np.bincount(idx.ravel(), minlength=w.E))
+    same = ~differ
+    # weights from the GPU's own scores: the score bound t propagated through w_i = alpha s_i / S,
+    # |dw_i| <= alpha (t / S + s_i k t / S^2), plus 4 ulp of the float32 steps
+    chosen = np.take_along_axis(s_ref, idx_ref.astype(np.int64), 1).astype(np.float64)
+    if w.norm:
+        S = chosen.sum(axis=1, keepdims=True) + w.eps
+        bound = w.alpha * (tol_s[:, None] / S + chosen * w.k * tol_s[:, None] / S**2)
+    else:
+        bound = w.alpha * tol_s[:, None] * np.ones_like(chosen)
+    bound = bound + 4 * np.spacing(np.abs(w_ref).astype(np.float32))
+    dev_w = np.abs(wt.astype(np.float64) - w_ref)
+    assert np.all(dev_w[same] <= bound[same]), f"weight deviation {dev_w[same].max():.3g}"
+    # per-token reference: the oracle's routing, or the GPU's where they differ at a near-tie
+    tokens = np.unique(np.concatenate([tokens, np.flatnonzero(differ)[:8]]))
+    r_idx = np.where(differ[:, None], idx, idx_ref)
+    r_w = np.where(differ[:, None], wt, w_ref)
+    table = H.expert_table(w, r_idx[tokens].ravel())
+    y_ref = oracle.forward_tokens(w, tokens, x, table, r_idx, r_w)
+    err = H.rel_err(H.as_f32(y[tokens]), y_ref)
+    print(f"  {w.name}: tokens={tokens.size} differ={int(differ.sum())} rel_err={err:.3g}", flush=True)
+    assert err <= H.TOL[w.dtype], err
+    return err
+
+
+@pytest.mark.parametrize("name", synth.WORKLOAD_ORDER)
+def test_forward_workload(name):
+    w = synth.WORKLOADS[name]
+    print(f"[forward] {name} N={w.N} D={w.D} E={w.E} k={w.k} d={w.d}", flush=True)
+    big = w.E * w.d * w.D > 50_000_000
+    wg, b, dev = H.device_weights(w, generate_on_device=big)
+    x = synth.x_host(w)
+    y, idx, wt, counts = H.gpu_forward(w, H.to_device(x), dev)
+    tokens = H.sample_tokens(w.N, 24 if big else w.N, seed=1)
+    _check_forward(w, x, wg, b, y, idx, wt, counts, tokens, big)
+
+
+SMALL = [
+    # several row tiles per expert, column tails on both GEMMs (D = 320, d = 192), ragged rows
+    dict(N=300, D=320, E=24, G=4, TG=2, k=5, d=192, n_shared=1, alpha=2.5),
+    dict(N=1000, D=512, E=8, G=1, TG=1, k=2, d=256, n_shared=1, alpha=1.0),
+    dict(N=77, D=256, E=32, G=8, TG=3, k=6, d=128, n_shared=2, alpha=2.5),
+    dict(N=129, D=192, E=12, G=1, TG=1, k=3, d=64, n_shared=0, alpha=2.5),
+    dict(N=50, D=256, E=16, G=4, TG=2, k=4, d=128, n_shared=1, alpha=2.5, norm=False),
+    dict(N=1, D=256, E=16, G=4, TG=2, k=4, d=128, n_shared=1, alpha=2.5),
+    dict(N=3, D=128, E=8, G=2, TG=1, k=1, d=64, n_shared=1, alpha=2.5),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"N{c['N']}-D{c['D']}-E{c['E']}-k{c['k']}-d{c['d']}")
+def test_forward_small_whole(case, dtype):
+    w = replace(synth.WORKLOADS["tiny_fp32"], name="small", dtype=dtype, seed=3, **case)
+    print(f"[small] {case} {dtype}", flush=True)
+    wg, b, dev = H.device_weights(w, generate_on_device=False)
+    x = synth.x_host(w)
+    y, idx, wt, counts = H.gpu_forward(w, H.to_device(x), dev)
+    _check_forward(w, x, wg, b, y, idx, wt, counts, np.arange(w.N), False)
+
+
+def test_forward_deterministic_and_permutation_equivariant():
+    """Same inputs, same bits; a permutation of the tokens permutes the output rows bit for bit."""
+    w = replace(synth.WORKLOADS["tiny_fp32"], name="perm", N=700, D=512, E=32, G=4, TG=2, k=6, d=256,
+                dtype="bf16", seed=5)
+    _, _, dev = H.device_weights(w, generate_on_device=False)
+    x = synth.x_host(w)
+    y1, i1, w1, _ = H.gpu_forward(w, H.to_device(x), dev)
+    y2, i2, w2, _ = H.gpu_forward(w, H.to_device(x), dev)
+    assert np.array_equal(y1, y2) and np.array_equal(i1, i2) and np.array_equal(w1, w2)
+    perm = np.random.default_rng(0).permutation(w.N)
+    y3, i3, w3, _ = H.gpu_forward(w, H.to_device(x[perm]), dev)
+    assert np.array_equal(y3, y1[perm]) and np.array_equal(i3, i1[perm]) and np.array_equal(w3, w1[perm])
+
+
+def test_device_generator_matches_host():
+    """The device build of the seeded generator reproduces the host build bit for bit."""
+    w = synth.WORKLOADS["glm5_prefill"]
+    _, _, dev = H.device_weights(w, generate_on_device=True)
+    for e in (0, 77, w.E - 1):
+        gu, dn = synth.expert_host(w, e)
+        assert np.array_equal(H.to_host(dev["gate_up"][e]), gu)
+        assert np.array_equal(H.to_host(dev["down"][e]), dn)
+    sg, su, sd = synth.shared_host(w)
+    assert np.array_equal(H.to_host(dev["sh_gate"]), sg)
+    assert np.array_equal(H.to_host(dev["sh_up"]), su)
+    assert np.array_equal(H.to_host(dev["sh_down"]), sd)

@@ -1,0 +1,184 @@
+"""GPU parity of the router and the dispatch against the oracle, through the C ABI.
+
+Bar: given the oracle's float32 scores, the GPU's expert ids and weights are bit-identical
+(moe_route with MOE_ROUTE_SCORES_IN); the GPU's own scores are within the float32 accumulation bound
+of the oracle's; counts, offsets, sorted_pair and inv_row are bit-identical.
+"""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import _harness as H
+
+pytestmark = pytest.mark.gpu
+
+ALL = synth.WORKLOAD_ORDER
+
+
+def _route_gpu(w, N, s_host=None, x_host=None, wg=None, b=None):
+    import torch
+
+    import sparse_moe_layer_gate_amd as moe
+
+    cfg = moe.config_of(w)
+    idx = torch.empty((N, w.k), dtype=torch.int32, device="cuda")
+    wt = torch.empty((N, w.k), dtype=torch.float32, device="cuda")
+    b_d = H.to_device(b)
+    if s_host is not None:
+        s_d = H.to_device(s_host)
+        moe.moe_route(cfg, N, None, None, b_d, s_d, idx, wt, flags=moe.MOE_ROUTE_SCORES_IN)
+    else:
+        s_d = torch.empty((N, w.E), dtype=torch.float32, device="cuda")
+        moe.moe_route(cfg, N, H.to_device(x_host), H.to_device(wg), b_d, s_d, idx, wt)
+    torch.cuda.synchronize()
+    return H.to_host(s_d), H.to_host(idx), H.to_host(wt)
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_selection_bitexact_given_scores(name):
+    w = synth.WORKLOADS[name]
+    print(f"[select] {name} N={w.N}", flush=True)
+    x = synth.x_host(w)
+    wg, b = synth.router_host(w)
+    s = oracle.scores(w, x, wg)
+    idx_ref, w_ref = oracle.select(w, s, b)
+    _, idx, wt = _route_gpu(w, w.N, s_host=s, b=b)
+    assert np.array_equal(idx, idx_ref)
+    assert np.array_equal(wt.view(np.uint32), w_ref.view(np.uint32))
+
+
+TIE_CASES = [
+    dict(E=16, G=4, TG=2, k=4),
+    dict(E=24, G=3, TG=2, k=5),
+    dict(E=288, G=1, TG=1, k=8),
+    dict(E=512, G=64, TG=8, k=32),
+    dict(E=256, G=8, TG=4, k=8, norm=False),
+    dict(E=64, G=8, TG=8, k=6),
+    dict(E=8, G=1, TG=1, k=1),
+]
+
+
+@pytest.mark.parametrize("case", TIE_CASES, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+@pytest.mark.parametrize("grid", [True, False])
+def test_selection_bitexact_tie_rich(case, grid):
+    """Scores on a 1/8 grid (ties everywhere) or continuous; bias on the same grid; signed zeros."""
+    w = replace(synth.WORKLOADS["tiny_fp32"], N=777, **case)
+    rng = np.random.default_rng(w.E + w.k)
+    if grid:
+        s = (rng.integers(0, 9, (w.N, w.E)) / 8.0).astype(np.float32)
+        b = (rng.integers(-1, 2, w.E) / 8.0).astype(np.float32)
+        b[::5] = -0.0
+    else:
+        s = rng.uniform(0, 1, (w.N, w.E)).astype(np.float32)
+        b = rng.uniform(-0.05, 0.05, w.E).astype(np.float32)
+    s[:7] = 0.0  # all-zero rows: eps keeps the weights at 0
+    idx_ref, w_ref = oracle.select(w, s, b)
+    _, idx, wt = _route_gpu(w, w.N, s_host=s, b=b)
+    assert np.array_equal(idx, idx_ref)
+    assert np.array_equal(wt.view(np.uint32), w_ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_scores_within_bound(name):
+    w = synth.WORKLOADS[name]
+    print(f"[scores] {name}", flush=True)
+    x = synth.x_host(w)
+    wg, b = synth.router_host(w)
+    s_ref = oracle.scores(w, x, wg)
+    s, idx, wt = _route_gpu(w, w.N, x_host=x, wg=wg, b=b)
+    tol = H.score_tolerance(w, x, wg)
+    err = np.abs(s.astype(np.float64) - s_ref)
+    assert np.all(err <= tol), f"max err {err.max():.3g}, worst ratio {(err / tol).max():.3g}"
+    # routing from the GPU's scores equals the oracle's except where the oracle's decision gap is
+    # within twice the score error bound
+    idx_ref, _ = oracle.select(w, s_ref, b)
+    margin = oracle.select_margin(w, s_ref, b)
+    differ = np.any(idx != idx_ref, axis=1)
+    assert np.all(margin[differ] <= 2 * tol.max(axis=1)[differ])
+
+
+def _dispatch_gpu(w, idx):
+    import torch
+
+    import sparse_moe_layer_gate_amd as moe
+
+    cfg = moe.config_of(w)
+    N = idx.shape[0]
+    ws = moe.alloc_workspace(cfg, N)
+    counts = torch.empty(w.E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(w.E + 1, dtype=torch.int32, device="cuda")
+    sp = torch.empty(N * w.k, dtype=torch.int32, device="cuda")
+    inv = torch.empty(N * w.k, dtype=torch.int32, device="cuda")
+    moe.moe_dispatch(cfg, N, H.to_device(np.ascontiguousarray(idx, np.int32)), counts, offsets, sp, inv, ws)
+    torch.cuda.synchronize()
+    return H.to_host(counts), H.to_host(offsets), H.to_host(sp), H.to_host(inv)
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_dispatch_bitexact(name):
+    w = synth.WORKLOADS[name]
+    x = synth.x_host(w)
+    wg, b = synth.router_host(w)
+    idx, _ = oracle.select(w, oracle.scores(w, x, wg), b)
+    got = _dispatch_gpu(w, idx)
+    ref = oracle.dispatch(w, idx)
+    for g, r, what in zip(got, ref, ["counts", "offsets", "sorted_pair", "inv_row"]):
+        assert np.array_equal(g, r), what
+
+
+@pytest.mark.parametrize("N,E,k,skew", [(1, 16, 4, 0), (255, 16, 4, 0), (257, 16, 4, 0), (70001, 160, 8, 0),
+                                        (5000, 256, 8, 1), (3000, 512, 32, 0), (1000, 7, 7, 1)])
+def test_dispatch_random(N, E, k, skew):
+    w = replace(synth.WORKLOADS["tiny_fp32"], N=N, E=E, G=1, TG=1, k=k)
+    rng = np.random.default_rng(N + E)
+    if skew:  # most tokens on the first k experts
+        base = np.arange(k)
+        idx = np.stack([base if rng.random() < 0.9 else rng.choice(E, k, replace=False) for _ in range(N)])
+    else:
+        idx = np.argsort(rng.random((N, E)), axis=1)[:, :k]
+    idx = idx.astype(np.int32)
+    got = _dispatch_gpu(w, idx)
+    ref = oracle.dispatch(w, idx)
+    for g, r, what in zip(got, ref, ["counts", "offsets", "sorted_pair", "inv_row"]):
+        assert np.array_equal(g, r), what
+
+
+def test_dispatch_leaves_out_invalid_ids():
+    w = replace(synth.WORKLOADS["tiny_fp32"], N=300, E=16, G=1, TG=1, k=4)
+    rng = np.random.default_rng(9)
+    idx = np.argsort(rng.random((300, 16)), axis=1)[:, :4].astype(np.int32)
+    bad = rng.random(idx.shape) < 0.05
+    idx[bad] = np.where(rng.random(bad.sum()) < 0.5, -1, 16)
+    counts, offsets, sp, inv = _dispatch_gpu(w, idx)
+    flat = idx.ravel()
+    valid = (flat >= 0) & (flat < 16)
+    assert np.array_equal(counts, np.bincount(flat[valid], minlength=16))
+    n_valid = int(valid.sum())
+    assert offsets[-1] == n_valid
+    assert np.all(inv[~valid] == -1)
+    assert np.array_equal(sp[:n_valid], np.flatnonzero(valid)[np.argsort(flat[valid], kind="stable")])
+    assert np.array_equal(inv[sp[:n_valid]], np.arange(n_valid))
+
+
+def test_zero_tokens_is_noop():
+    import torch
+
+    import sparse_moe_layer_gate_amd as moe
+
+    w = synth.WORKLOADS["tiny_fp32"]
+    cfg = moe.config_of(w)
+    e = torch.empty(0, device="cuda")
+    z = torch.zeros((0, w.k), dtype=torch.int32, device="cuda")
+    moe.moe_route(cfg, 0, None, None, torch.zeros(w.E, device="cuda"), torch.empty((0, w.E), device="cuda"), z,
+                  torch.empty((0, w.k), device="cuda"), flags=moe.MOE_ROUTE_SCORES_IN)
+    ws = moe.alloc_workspace(cfg, 0)
+    counts = torch.full((w.E,), 7, dtype=torch.int32, device="cuda")
+    offsets = torch.full((w.E + 1,), 7, dtype=torch.int32, device="cuda")
+    moe.moe_dispatch(cfg, 0, z, counts, offsets, torch.empty(0, dtype=torch.int32, device="cuda"),
+                     torch.empty(0, dtype=torch.int32, device="cuda"), ws)
+    torch.cuda.synchronize()
+    assert int(counts.abs().sum()) == 0 and int(offsets.abs().sum()) == 0
+    del e
