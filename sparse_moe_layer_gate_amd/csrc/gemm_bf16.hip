@@ -1,0 +1,301 @@
+// Grouped bf16 expert GEMMs for token-rich (prefill) batches.
+//
+// Same products as the generic grouped kernels ("MoE Forward", eq. E_i: the gate_up GEMM with the
+// SwiGLU applied in registers, and the down GEMM scaled by the mixture weight w_{n,i}), laid out for
+// gfx950:
+//  - block tile BM x 256 with BM = 256 or 128, four waves; a wave owns (BM / WM) x (256 / WN) outputs
+//    as TM x TN tiles of v_mfma_f32_32x32x16_bf16 (accumulators in AGPRs);
+//  - operands go global -> LDS directly (global_load_lds_dwordx4: lane l of a wave writes bytes
+//    [16 l, 16 l + 16) of a 1 KiB run), no register staging;
+//  - LDS rows are BK bf16 long, unpadded; the 16-byte chunks of a row are XOR-swizzled by the row's
+//    position so that the MFMA operand reads (32 rows at one k offset) hit distinct banks;
+//  - STAGES-deep ring of K steps: loads for step t + STAGES - 1 are in flight while step t computes;
+//  - 32-row MFMA sub-tiles past a tile's valid rows are skipped, so a sparsely filled tile (a rarely
+//    chosen expert) costs little MFMA time.
+#include <hip/hip_runtime.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+#ifndef MOE_PF_GROUP_ROWS
+#define MOE_PF_GROUP_ROWS 4
+#endif
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ inline uint16_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ inline float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+// s_waitcnt with vmcnt = N and the other counters left at their maximum (gfx9 encoding).
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int BM, int BK, int STAGES, bool GATE_UP>
+struct PrefillTile {
+  static constexpr int BN = 256;
+  static constexpr int WM = BM == 256 ? 2 : 1, WN = 4 / WM;
+  static constexpr int WAVE_M = BM / WM, WAVE_N = BN / WN;
+  static constexpr int TM = WAVE_M / 32, TN = WAVE_N / 32;
+  static constexpr int ROWB = BK * 2;        // bytes per LDS row
+  static constexpr int CPR = BK / 8;         // 16-byte chunks per row
+  static constexpr int NA = BM * CPR / 256;  // direct loads per thread per K step (A)
+  static constexpr int NB = BN * CPR / 256;  // (B)
+  static constexpr int LPS = NA + NB;
+  static constexpr int STAGE_BYTES = (BM + BN) * ROWB;
+  static constexpr int COLS = GATE_UP ? BN / 2 : BN;  // output columns per block
+  static_assert(TN % 2 == 0, "gate_up pairs gate and up column tiles inside a wave");
+  static_assert(CPR == 8 || CPR == 4, "BK is 64 or 32");
+
+  // Chunk swizzle: the 16-byte chunk c of LDS row r is stored in slot c ^ swz(r). swz depends on
+  // r mod 32 only, and any 8 (and any aligned 16) consecutive rows get distinct slots, so the MFMA
+  // operand reads (32 rows x one chunk) are free of bank conflicts for 8- or 16-lane LDS passes.
+  __device__ static int swz(int r) {
+    r &= 31;
+    if (CPR == 8) return (r ^ (r >> 3)) & 7;
+    return ((r >> 1) ^ (r >> 3)) & 3;
+  }
+
+  // One K step's direct loads: load q of wave w fills the operand's chunks [(4 q + w) 64, + 64).
+  __device__ static void issue(char* lds, const uint16_t* const (&srcA)[NA], const uint16_t* const (&srcB)[NB],
+                               int kstep, int wave) {
+    char* st = lds + (kstep % STAGES) * STAGE_BYTES;
+    const int k0 = kstep * BK;
+#pragma unroll
+    for (int q = 0; q < NA; ++q)
+      __builtin_amdgcn_global_load_lds((const void*)(srcA[q] + k0), (lds_void*)(st + (q * 4 + wave) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int q = 0; q < NB; ++q)
+      __builtin_amdgcn_global_load_lds((const void*)(srcB[q] + k0), (lds_void*)(st + BM * ROWB + (q * 4 + wave) * 1024),
+                                       16, 0, 0);
+  }
+
+  __device__ static int b_row(int j, int wn) {
+    if (GATE_UP) return (j < TN / 2 ? 0 : BN / 2) + wn * (WAVE_N / 2) + (j % (TN / 2)) * 32;
+    return wn * WAVE_N + j * 32;
+  }
+
+  // The K loop for a wave whose first MI 32-row sub-tiles hold valid rows (MI = 0: loads only).
+  template <int MI>
+  __device__ static __attribute__((always_inline)) void run(char* lds, const uint16_t* const (&srcA)[NA],
+                                                            const uint16_t* const (&srcB)[NB], f32x16 (&acc)[TM][TN],
+                                                            int nk, int wave, int lane, int wm, int wn) {
+    const int sw = swz(lane & 31);
+    const int a_off = (wm * WAVE_M + (lane & 31)) * ROWB;
+    int b_off[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) b_off[j] = BM * ROWB + (b_row(j, wn) + (lane & 31)) * ROWB;
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+      if (s < nk) issue(lds, srcA, srcB, s, wave);
+    for (int kt = 0; kt < nk; ++kt) {
+      // Step kt's direct loads are this wave's oldest outstanding VMEM ops; once every wave has waited
+      // for its own and met at the barrier, step kt is in LDS. The barrier also ends every wave's reads
+      // of the stage that the next issue() refills (they fed MFMAs of step kt - 1). A plain s_barrier:
+      // __syncthreads() would add a vmcnt(0) wait and drain the prefetches of later steps.
+      if (kt + STAGES - 2 < nk)
+        wait_vmcnt<(STAGES - 2) * LPS>();
+      else
+        wait_vmcnt<0>();
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_barrier();
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      if (kt + STAGES - 1 < nk) issue(lds, srcA, srcB, kt + STAGES - 1, wave);
+      if (MI == 0) continue;
+      const char* st = lds + (kt % STAGES) * STAGE_BYTES;
+      bf16x8 af[2][MI > 0 ? MI : 1], bfr[2][TN];
+      auto load_frags = [&](int kk, int buf) {
+        const int coff = ((2 * kk + (lane >> 5)) ^ sw) * 16;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) bfr[buf][j] = *(const bf16x8*)(st + b_off[j] + coff);
+#pragma unroll
+        for (int i = 0; i < MI; ++i) af[buf][i] = *(const bf16x8*)(st + a_off + i * 32 * ROWB + coff);
+      };
+      load_frags(0, 0);
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        if (kk + 1 < BK / 16) load_frags(kk + 1, (kk + 1) & 1);
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk & 1][i], bfr[kk & 1][j], acc[i][j], 0, 0, 0);
+      }
+      schedule<MI>();
+    }
+  }
+
+  // Instruction order of one K step: the first slice's operand reads, then each slice's MFMAs with the
+  // next slice's reads spread between them, so LDS latency hides under MFMA work.
+  template <int MI>
+  __device__ static __attribute__((always_inline)) void schedule() {
+#ifndef MOE_PF_NO_SCHED
+    constexpr int R = MI + TN;   // LDS reads per slice
+    constexpr int M = MI * TN;   // MFMAs per slice
+    constexpr int PER = M / R > 0 ? M / R : 1;
+    __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+#pragma unroll
+    for (int kk = 0; kk + 1 < BK / 16; ++kk) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      if (M > PER * R) __builtin_amdgcn_sched_group_barrier(0x008, M - PER * R, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, M, 0);
+#endif
+  }
+};
+
+template <int BM, int BK, int STAGES, bool GATE_UP>
+__global__ __launch_bounds__(256, 1) void grouped_bf16_lds(GroupedArgs a, int ncol_max) {
+  using T = PrefillTile<BM, BK, STAGES, GATE_UP>;
+  constexpr int BN = T::BN, CPR = T::CPR, NA = T::NA, NB = T::NB, TM = T::TM, TN = T::TN;
+  constexpr int WAVE_M = T::WAVE_M, WAVE_N = T::WAVE_N;
+
+  __shared__ __attribute__((aligned(1024))) char lds[STAGES * T::STAGE_BYTES];
+  __shared__ float wrow[BM];
+
+  // Rasterization: logical ids walk GR row tiles down a column before moving right, so the blocks
+  // one XCD runs together share GR-fold the B slices and (32 / GR)-fold the A slices.
+  const int64_t L = xcd_logical_block();
+  constexpr int GR = MOE_PF_GROUP_ROWS;
+  const int64_t sg = L / ((int64_t)GR * ncol_max), within = L % ((int64_t)GR * ncol_max);
+  const int64_t tile_id = sg * GR + within % GR;
+  const int ct = (int)(within / GR);
+  if (tile_id >= *a.n_tiles) return;
+  const Tile tile = a.tiles[tile_id];
+  const ExpertProblem P = pick_problem(a, tile.problem);
+  const int col0 = ct * T::COLS;
+  if (col0 >= P.ncols) return;
+
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wm = wave / T::WN, wn = wave % T::WN;
+
+  // Global source of each direct load: LDS chunk p is row p / CPR, slot p % CPR, which holds the
+  // row's logical chunk slot ^ swz(row).
+  const uint16_t* srcA[NA];
+  const uint16_t* srcB[NB];
+#pragma unroll
+  for (int q = 0; q < NA; ++q) {
+    const int p = (q * 4 + wave) * 64 + lane;
+    const int r = p / CPR, c = (p % CPR) ^ T::swz(r);
+    int64_t g = (int64_t)tile.row_start + min(r, tile.rows - 1);
+    if (P.gather) g = a.sorted_pair[g] / a.k;
+    srcA[q] = (const uint16_t*)P.A + g * P.lda + 8 * c;
+  }
+#pragma unroll
+  for (int q = 0; q < NB; ++q) {
+    const int p = (q * 4 + wave) * 64 + lane;
+    const int r = p / CPR, c = (p % CPR) ^ T::swz(r);
+    const uint16_t* base;
+    int col;
+    if (GATE_UP) {
+      base = (const uint16_t*)(r < BN / 2 ? P.B0 : P.B1);
+      col = min(col0 + (r % (BN / 2)), P.ncols - 1);
+    } else {
+      base = (const uint16_t*)P.B0;
+      col = min(col0 + r, P.ncols - 1);
+    }
+    srcB[q] = base + (int64_t)tile.expert * P.b_stride + (int64_t)col * P.K + 8 * c;
+  }
+  if (!GATE_UP && t < BM) {
+    const int r = min(t, tile.rows - 1);
+    wrow[t] = P.scale_rows ? a.topk_w[a.sorted_pair[tile.row_start + r]] : 1.0f;
+  }
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nk = P.K / BK;
+  const int live_m = tile.rows - wm * WAVE_M;  // valid rows of this wave's slab
+  const int mi = live_m <= 0 ? 0 : min(TM, (live_m + 31) / 32);
+#define MOE_PF_RUN run
+  switch (mi) {
+    case 0: T::template MOE_PF_RUN<0>(lds, srcA, srcB, acc, nk, wave, lane, wm, wn); break;
+    case 1: T::template MOE_PF_RUN<1>(lds, srcA, srcB, acc, nk, wave, lane, wm, wn); break;
+    case 2: T::template MOE_PF_RUN<(TM >= 2 ? 2 : 1)>(lds, srcA, srcB, acc, nk, wave, lane, wm, wn); break;
+    case 3: T::template MOE_PF_RUN<(TM >= 3 ? 3 : 1)>(lds, srcA, srcB, acc, nk, wave, lane, wm, wn); break;
+    default: T::template MOE_PF_RUN<TM>(lds, srcA, srcB, acc, nk, wave, lane, wm, wn); break;
+  }
+#undef MOE_PF_RUN
+
+  // 32x32 C layout: lane holds column lane % 32, rows 8 (r / 4) + 4 (lane / 32) + r % 4.
+  uint16_t* out = (uint16_t*)P.out;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    if (i >= mi) continue;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = wm * WAVE_M + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      if (row >= tile.rows) continue;
+      const int64_t orow = (int64_t)tile.row_start + row;
+      if (GATE_UP) {
+#pragma unroll
+        for (int j = 0; j < TN / 2; ++j) {
+          const int col = col0 + wn * (WAVE_N / 2) + j * 32 + (lane & 31);
+          if (col < P.ncols) out[orow * P.ldo + col] = bf16_rne(silu_mul(acc[i][j][r], acc[i][j + TN / 2][r]));
+        }
+      } else {
+        const float sc = wrow[row];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int col = col0 + wn * WAVE_N + j * 32 + (lane & 31);
+          if (col < P.ncols) out[orow * P.ldo + col] = bf16_rne(acc[i][j][r] * sc);
+        }
+      }
+    }
+  }
+}
+
+#ifndef MOE_PF_BK
+#define MOE_PF_BK 64
+#endif
+#ifndef MOE_PF_GROUP_ROWS
+#define MOE_PF_GROUP_ROWS 4
+#endif
+#ifndef MOE_PF_STAGES
+#define MOE_PF_STAGES 2
+#endif
+
+template <bool GATE_UP>
+hipError_t launch_bm(int bm, const GroupedArgs& a, int64_t max_tile_count, hipStream_t s) {
+  constexpr int COLS = GATE_UP ? 128 : 256;
+  int nc = 0;
+  for (int p = 0; p < 2; ++p)
+    if (a.prob[p].out) nc = max(nc, (a.prob[p].ncols + COLS - 1) / COLS);
+  int64_t blocks = (max_tile_count * nc + 7) / 8 * 8;
+  if (blocks == 0) return hipSuccess;
+  if (bm == 256)
+    hipLaunchKernelGGL((grouped_bf16_lds<256, MOE_PF_BK, MOE_PF_STAGES, GATE_UP>), dim3((unsigned)blocks), dim3(256),
+                       0, s, a, nc);
+  else
+    hipLaunchKernelGGL((grouped_bf16_lds<128, MOE_PF_BK, MOE_PF_STAGES, GATE_UP>), dim3((unsigned)blocks), dim3(256),
+                       0, s, a, nc);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bf16_prefill(bool gate_up, int bm, const GroupedArgs& a, int64_t max_tile_count, hipStream_t s) {
+  return gate_up ? launch_bm<true>(bm, a, max_tile_count, s) : launch_bm<false>(bm, a, max_tile_count, s);
+}
+
+}  // namespace moe

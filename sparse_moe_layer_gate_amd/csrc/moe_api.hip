@@ -254,6 +254,7 @@ moe_status moe_forward(const moe_config* cfg, int64_t N, const void* x, const mo
   // gate_up + SwiGLU: routed rows gather x through sorted_pair; the shared expert reads x in order
   g.tiles = at<Tile>(ws, L.tiles0);
   g.n_tiles = at<int32_t>(ws, L.ntiles);
+  g.bm = L.bm0;
   g.prob[0] = ExpertProblem{x, D, 1, wt->gate_up, (const char*)wt->gate_up + es * (int64_t)d * D, 2LL * d * D, D, d,
                             at<void>(ws, L.H), d, 0};
   if (shared)
@@ -262,6 +263,7 @@ moe_status moe_forward(const moe_config* cfg, int64_t N, const void* x, const mo
   // down + mixture weight (routed) / weight 1 (shared)
   g.tiles = at<Tile>(ws, L.tiles1);
   g.n_tiles = at<int32_t>(ws, L.ntiles) + 1;
+  g.bm = L.bm1;
   g.prob[0] = ExpertProblem{at<void>(ws, L.H), d, 0, wt->down, nullptr, (int64_t)D * d, d, D, at<void>(ws, L.Y), D, 1};
   if (shared)
     g.prob[1] = ExpertProblem{at<void>(ws, L.Hsh), dsh, 0, wt->sh_down, nullptr, 0, dsh, D, at<void>(ws, L.Ysh), D, 0};

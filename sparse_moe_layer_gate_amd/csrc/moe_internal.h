@@ -72,17 +72,47 @@ struct ExpertProblem {
 };
 struct GroupedArgs {
   ExpertProblem prob[2];
+  int bm;  // rows per tile of the tile list this launch walks
   const Tile* tiles;
   const int32_t* n_tiles;
   const int32_t* sorted_pair;
   const float* topk_w;
   int k;
 };
+// Field-wise select keeps a problem descriptor in scalar registers (a dynamically indexed
+// kernel-argument array would be copied to scratch).
+__device__ inline ExpertProblem pick_problem(const GroupedArgs& a, int p) {
+  ExpertProblem r;
+  const ExpertProblem& x = a.prob[0];
+  const ExpertProblem& y = a.prob[1];
+  r.A = p ? y.A : x.A;
+  r.lda = p ? y.lda : x.lda;
+  r.gather = p ? y.gather : x.gather;
+  r.B0 = p ? y.B0 : x.B0;
+  r.B1 = p ? y.B1 : x.B1;
+  r.b_stride = p ? y.b_stride : x.b_stride;
+  r.K = p ? y.K : x.K;
+  r.ncols = p ? y.ncols : x.ncols;
+  r.out = p ? y.out : x.out;
+  r.ldo = p ? y.ldo : x.ldo;
+  r.scale_rows = p ? y.scale_rows : x.scale_rows;
+  return r;
+}
+
+// Block id -> logical work id. The hardware deals workgroups to the 8 XCDs round-robin; this remap
+// gives each XCD a contiguous run of logical ids, so the column tiles of one row tile (which share
+// the A rows) and neighbouring row tiles of one expert (which share B) meet in one L2.
+__device__ inline int64_t xcd_logical_block() {
+  const int64_t b = blockIdx.x, nb = gridDim.x;  // nb is a multiple of 8
+  return (b & 7) * (nb >> 3) + (b >> 3);
+}
+
 // Upper bound on tiles for a tile list with bm rows per tile.
 int64_t max_tiles(int64_t N, int k, int E, int n_shared_problem, int bm);
 int gemm_bm(int dtype, int64_t N, int k, int E);  // rows per tile the forward will use
 hipError_t launch_gate_up(int dtype, const GroupedArgs& a, int64_t max_tile_count, hipStream_t s);
 hipError_t launch_down(int dtype, const GroupedArgs& a, int64_t max_tile_count, hipStream_t s);
+hipError_t launch_bf16_prefill(bool gate_up, int bm, const GroupedArgs& a, int64_t max_tile_count, hipStream_t s);
 
 // ---- combine ----
 hipError_t launch_combine(int dtype, const void* Y, const void* Ysh, const int32_t* inv_row, int64_t N, int k, int D,
