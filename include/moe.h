@@ -103,10 +103,15 @@ size_t moe_workspace_size(const moe_config* cfg, int64_t N);
  *   scores   [N, E] float32: written with s (default) or read (MOE_ROUTE_SCORES_IN)
  *   topk_idx [N, k] int32 out: the chosen experts in slot order
  *   topk_w   [N, k] float32 out: their weights, alpha included
- * Given the same float32 scores, indices and weights are bit-identical to a float32 evaluation in the
- * order stated above (correctly rounded add, divide and multiply). */
+ *   workspace, ws_bytes: scratch of at least moe_workspace_size(cfg, N) bytes (unused, may be NULL,
+ *            with MOE_ROUTE_SCORES_IN)
+ * The logits are float32 dot products (bf16 activations: exact products of x with an exact three-piece
+ * bf16 split of w_router, accumulated in float32 on the matrix cores). Given the same float32 scores,
+ * indices and weights are bit-identical to a float32 evaluation in the order stated above (correctly
+ * rounded add, divide and multiply). */
 moe_status moe_route(const moe_config* cfg, int64_t N, const void* x, const float* w_router, const float* e_bias,
-                     float* scores, uint32_t flags, int32_t* topk_idx, float* topk_w, void* stream);
+                     float* scores, uint32_t flags, int32_t* topk_idx, float* topk_w, void* workspace,
+                     size_t ws_bytes, void* stream);
 
 /* Token-choice dispatch: per-expert token lists in the per-expert loop form of "GLM-5 . Mixture of
  * experts", as counts, an exclusive scan and a stable placement (tokens ascending inside each expert).

@@ -64,7 +64,7 @@ def lib():
         L.moe_check_config.restype = ctypes.c_int
         L.moe_workspace_size.argtypes = [cp, i64]
         L.moe_workspace_size.restype = ctypes.c_size_t
-        L.moe_route.argtypes = [cp, i64, vp, vp, vp, vp, u32, vp, vp, vp]
+        L.moe_route.argtypes = [cp, i64, vp, vp, vp, vp, u32, vp, vp, vp, ctypes.c_size_t, vp]
         L.moe_route.restype = ctypes.c_int
         L.moe_dispatch.argtypes = [cp, i64, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.moe_dispatch.restype = ctypes.c_int
@@ -154,8 +154,10 @@ def alloc_workspace(cfg: MoeConfig, N: int, device="cuda"):
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
-def moe_route(cfg: MoeConfig, N: int, x, w_router, e_bias, scores, topk_idx, topk_w, flags: int = 0, stream=None):
-    """Router on the GPU. With flags = MOE_ROUTE_SCORES_IN, `scores` [N, E] is read and x / w_router ignored."""
+def moe_route(cfg: MoeConfig, N: int, x, w_router, e_bias, scores, topk_idx, topk_w, flags: int = 0,
+              workspace=None, stream=None):
+    """Router on the GPU. With flags = MOE_ROUTE_SCORES_IN, `scores` [N, E] is read and x / w_router /
+    workspace are ignored; otherwise `workspace` (uint8, moe_workspace_size bytes) is required."""
     import torch
 
     E, D, k = cfg.n_routed_experts, cfg.hidden_size, cfg.num_experts_per_tok
@@ -169,6 +171,8 @@ def moe_route(cfg: MoeConfig, N: int, x, w_router, e_bias, scores, topk_idx, top
         int(flags),
         _ptr(topk_idx, "topk_idx", torch.int32, (N, k)),
         _ptr(topk_w, "topk_w", torch.float32, (N, k)),
+        _ptr(workspace, "workspace", torch.uint8, required=not scores_in),
+        0 if workspace is None else workspace.numel(),
         _stream(stream))
     _check(st, "moe_route")
 

@@ -43,7 +43,9 @@ size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Workspace {
   size_t scores, idx, w, chunk_counts, chunk_base, counts, offsets, sorted_pair, inv_row, tiles0, tiles1, ntiles;
+  size_t w3, part, route_total;  // router: split weight, logit partials; bytes moe_route needs
   size_t H, Hsh, Y, Ysh, total;
+  RouterPlan rp;
   int64_t max_tiles0, max_tiles1;
   int bm0, bm1;
 };
@@ -59,12 +61,17 @@ Workspace layout(const moe_config* c, int64_t N) {
   w.bm1 = w.bm0;
   w.max_tiles0 = max_tiles(N, (int)k, (int)E, shp, w.bm0);
   w.max_tiles1 = max_tiles(N, (int)k, (int)E, shp, w.bm1);
+  w.rp = router_plan(c->dtype, N, (int)D, (int)E);
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at = o;
     o = align_up(o + bytes);
     return at;
   };
+  // router scratch first: moe_route needs only this prefix
+  w.w3 = take(w.rp.split ? sizeof(uint16_t) * 3 * E * D : 0);
+  w.part = take(sizeof(float) * w.rp.ks * N * E);
+  w.route_total = o;
   w.scores = take(sizeof(float) * N * E);
   w.idx = take(sizeof(int32_t) * N * k);
   w.w = take(sizeof(float) * N * k);
@@ -126,12 +133,19 @@ const char* kStageNames[ST_COUNT_STAGES] = {"router_split", "router_logits", "ro
   } while (0)
 
 moe_status route_impl(const moe_config* c, int64_t N, const void* x, const float* wg, const float* bias,
-                      float* scores, uint32_t flags, int32_t* idx, float* w, hipStream_t s) {
-  const int E = c->n_routed_experts;
-  if (!(flags & MOE_ROUTE_SCORES_IN))
-    MOE_TRY(ST_LOGITS, launch_logits(c->dtype, x, wg, nullptr, N, c->hidden_size, E, scores, s));
-  MOE_TRY(ST_SELECT, launch_select(scores, bias, N, E, c->n_group, c->topk_group, c->num_experts_per_tok,
-                                   c->routed_scaling_factor, c->norm_topk_prob, c->eps, idx, w, s));
+                      float* scores, uint32_t flags, int32_t* idx, float* w, void* ws, const Workspace& L,
+                      hipStream_t s) {
+  const int E = c->n_routed_experts, D = c->hidden_size;
+  float* part = nullptr;
+  if (!(flags & MOE_ROUTE_SCORES_IN)) {
+    uint16_t* w3 = at<uint16_t>(ws, L.w3);
+    part = at<float>(ws, L.part);
+    if (L.rp.split) MOE_TRY(ST_ROUTER_SPLIT, launch_router_split(wg, E, D, w3, s));
+    MOE_TRY(ST_LOGITS, launch_logits(c->dtype, L.rp, x, wg, w3, N, D, E, part, s));
+  }
+  MOE_TRY(ST_SELECT, launch_select(scores, part, L.rp.ks, bias, N, E, c->n_group, c->topk_group,
+                                   c->num_experts_per_tok, c->routed_scaling_factor, c->norm_topk_prob, c->eps, idx, w,
+                                   s));
   return MOE_OK;
 }
 
@@ -180,15 +194,21 @@ size_t moe_workspace_size(const moe_config* cfg, int64_t N) {
 }
 
 moe_status moe_route(const moe_config* cfg, int64_t N, const void* x, const float* w_router, const float* e_bias,
-                     float* scores, uint32_t flags, int32_t* topk_idx, float* topk_w, void* stream) {
+                     float* scores, uint32_t flags, int32_t* topk_idx, float* topk_w, void* workspace, size_t ws_bytes,
+                     void* stream) {
   moe_status st = check_cfg(cfg);
   if (st != MOE_OK) return st;
   if ((st = check_n(cfg, N)) != MOE_OK) return st;
   if (flags & ~MOE_ROUTE_SCORES_IN) return MOE_ERR_INVALID_ARG;
   if (N == 0) return MOE_OK;
   if (!e_bias || !scores || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
-  if (!(flags & MOE_ROUTE_SCORES_IN) && (!x || !w_router)) return MOE_ERR_INVALID_ARG;
-  return route_impl(cfg, N, x, w_router, e_bias, scores, flags, topk_idx, topk_w, (hipStream_t)stream);
+  const Workspace L = layout(cfg, N);
+  if (!(flags & MOE_ROUTE_SCORES_IN)) {
+    if (!x || !w_router) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(w_router)) return MOE_ERR_INVALID_ARG;
+    if (!workspace || ws_bytes < L.route_total || !aligned16(workspace)) return MOE_ERR_WORKSPACE;
+  }
+  return route_impl(cfg, N, x, w_router, e_bias, scores, flags, topk_idx, topk_w, workspace, L, (hipStream_t)stream);
 }
 
 moe_status moe_dispatch(const moe_config* cfg, int64_t N, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
@@ -242,7 +262,7 @@ moe_status moe_forward(const moe_config* cfg, int64_t N, const void* x, const mo
   int32_t* sorted_pair = at<int32_t>(ws, L.sorted_pair);
   int32_t* inv_row = at<int32_t>(ws, L.inv_row);
 
-  if ((st = route_impl(cfg, N, x, wt->w_router, wt->e_bias, at<float>(ws, L.scores), 0, idx, w, s)) != MOE_OK)
+  if ((st = route_impl(cfg, N, x, wt->w_router, wt->e_bias, at<float>(ws, L.scores), 0, idx, w, ws, L, s)) != MOE_OK)
     return st;
   if ((st = dispatch_impl(cfg, N, idx, counts, at<int32_t>(ws, L.offsets), sorted_pair, inv_row, ws, L, s)) != MOE_OK)
     return st;

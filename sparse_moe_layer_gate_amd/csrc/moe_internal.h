@@ -37,11 +37,18 @@ void prof_after(int stage, hipStream_t s);
 constexpr int kDispatchChunk = 256;  // tokens per dispatch block
 
 // ---- router ----
-hipError_t launch_router_split(const float* wg, int E, int D, uint16_t* wsplit, hipStream_t s);
-hipError_t launch_logits(int dtype, const void* x, const float* wg, const uint16_t* wsplit, int64_t N, int D, int E,
-                         float* scores, hipStream_t s);
-hipError_t launch_select(const float* scores, const float* bias, int64_t N, int E, int G, int TG, int k, float alpha,
-                         int norm, float eps, int32_t* idx, float* w, hipStream_t s);
+struct RouterPlan {
+  bool split;  // bf16 activations: the router weight runs as three bf16 pieces on the bf16 matrix cores
+  int ks;      // partial sums per logit (split of the hidden dimension)
+  int kchunk;  // hidden elements per split (a multiple of 32)
+};
+RouterPlan router_plan(int dtype, int64_t N, int D, int E);
+hipError_t launch_router_split(const float* wg, int E, int D, uint16_t* w3, hipStream_t s);
+hipError_t launch_logits(int dtype, const RouterPlan& p, const void* x, const float* wg, const uint16_t* w3, int64_t N,
+                         int D, int E, float* part, hipStream_t s);
+// part == nullptr: scores are an input; otherwise scores are formed from the KS partials and written.
+hipError_t launch_select(float* scores, const float* part, int KS, const float* bias, int64_t N, int E, int G, int TG,
+                         int k, float alpha, int norm, float eps, int32_t* idx, float* w, hipStream_t s);
 
 // ---- dispatch ----
 struct TileSpec {

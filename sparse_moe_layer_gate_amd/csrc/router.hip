@@ -1,8 +1,16 @@
-// Router kernels: the gate GEMM with its sigmoid, and the selection / weight kernel.
+// Router kernels: the gate GEMM, and the selection / weight kernel.
 //
 // "Group Router" (GLM-4.5), How it works: s = sigmoid(x W_g^T) with a bias-free float32 gate;
 // s' = s + b chooses the experts; groups are scored by their two largest s'; topk_group groups
 // survive; the top-k by s' inside them are taken; w = alpha * s / (sum s + eps) from the raw s.
+//
+// The gate GEMM writes float32 logits split along the hidden dimension (KS partial sums per logit);
+// the selection kernel adds the partials in a fixed order, applies the sigmoid and writes the scores.
+//  - bf16 activations: the float32 router weight is split exactly into three bf16 pieces,
+//    W = hi + mid + lo (each piece the bf16 rounding of what the previous ones left), so every product
+//    x * piece is exact in float32 and the bf16 matrix cores accumulate x W in float32 at 3x the bf16
+//    work instead of running the 16x slower float32 matrix path.
+//  - float32 activations: v_mfma_f32_16x16x4_f32 (exact float32 products, float32 accumulation).
 #include <hip/hip_runtime.h>
 
 #include "moe_internal.h"
@@ -11,31 +19,162 @@ namespace moe {
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ inline float load_as_f32(const float* p, int64_t i) { return p[i]; }
 __device__ inline float load_as_f32(const uint16_t* p, int64_t i) {
   return __uint_as_float((uint32_t)p[i] << 16);  // bf16 -> f32 is exact
 }
 
+__device__ inline uint16_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ inline float bf16_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // ---------------------------------------------------------------------------------------------
-// Gate GEMM: scores[n, e] = sigmoid(sum_t x[n, t] * W_g[e, t]) in float32 on the fp32 matrix cores
-// (v_mfma_f32_16x16x4_f32: exact float32 products, float32 accumulation).
+// W (float32) -> hi, mid, lo (bf16), stored as three [E, D] matrices. Each residual is exact in
+// float32, so hi + mid + lo == W.
+__global__ __launch_bounds__(256) void split_kernel(const float* __restrict__ wg, int64_t count,
+                                                    uint16_t* __restrict__ w3) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count; i += (int64_t)gridDim.x * 256) {
+    const float w = wg[i];
+    const uint16_t hi = bf16_rne(w);
+    const float r1 = __fsub_rn(w, bf16_f32(hi));
+    const uint16_t mid = bf16_rne(r1);
+    const float r2 = __fsub_rn(r1, bf16_f32(mid));
+    w3[i] = hi;
+    w3[count + i] = mid;
+    w3[2 * count + i] = bf16_rne(r2);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// bf16 gate GEMM: part[ks, n, e] = sum over the ks-th hidden range of x[n, t] (lo + mid + hi)[e, t].
+// Block tile 64 tokens x 128 experts, K step 32, two-stage LDS ring fed by global_load_lds_dwordx4
+// (the swizzled chunk layout of the expert GEMMs); 4 waves in 2 x 2, each 32 tokens x 64 experts
+// as 1 x 2 tiles of v_mfma_f32_32x32x16_bf16 per piece.
+constexpr int RB_BM = 64, RB_BN = 128, RB_BK = 32, RB_ROWB = RB_BK * 2, RB_CPR = 4;
+constexpr int RB_A_BYTES = RB_BM * RB_ROWB, RB_B_BYTES = 3 * RB_BN * RB_ROWB;
+constexpr int RB_STAGE = RB_A_BYTES + RB_B_BYTES;
+constexpr int RB_NB = 3 * RB_BN * RB_CPR / 256;  // B loads per thread per K step (A: 1)
+
+__device__ inline int rb_swz(int r) {
+  r &= 31;
+  return ((r >> 1) ^ (r >> 3)) & 3;
+}
+
+__global__ __launch_bounds__(256) void logits_bf16x3_kernel(const uint16_t* __restrict__ x,
+                                                            const uint16_t* __restrict__ w3, int64_t N, int D, int E,
+                                                            int kchunk, float* __restrict__ part) {
+  __shared__ __attribute__((aligned(1024))) char lds[2 * RB_STAGE];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int64_t n0 = (int64_t)blockIdx.x * RB_BM;
+  const int e0 = blockIdx.y * RB_BN;
+  const int ks = blockIdx.z;
+  const int kbeg = ks * kchunk;
+  const int nk = min(kchunk, D - kbeg) / RB_BK;
+
+  // direct-load sources (fixed rows; the K offset advances)
+  const uint16_t* srcA;
+  {
+    const int p = wave * 64 + lane, r = p / RB_CPR, c = (p % RB_CPR) ^ rb_swz(r);
+    const int64_t n = min(n0 + r, N - 1);
+    srcA = x + n * D + kbeg + 8 * c;
+  }
+  const uint16_t* srcB[RB_NB];
+#pragma unroll
+  for (int q = 0; q < RB_NB; ++q) {
+    const int p = (q * 4 + wave) * 64 + lane;
+    const int piece = p / (RB_BN * RB_CPR), rr = (p % (RB_BN * RB_CPR)) / RB_CPR;
+    const int c = (p % RB_CPR) ^ rb_swz(rr);
+    const int e = min(e0 + rr, E - 1);
+    srcB[q] = w3 + (int64_t)piece * E * D + (int64_t)e * D + kbeg + 8 * c;
+  }
+  auto issue = [&](int kstep) {
+    char* st = lds + (kstep & 1) * RB_STAGE;
+    const int k0 = kstep * RB_BK;
+    __builtin_amdgcn_global_load_lds((const void*)(srcA + k0), (lds_void*)(st + wave * 1024), 16, 0, 0);
+#pragma unroll
+    for (int q = 0; q < RB_NB; ++q)
+      __builtin_amdgcn_global_load_lds((const void*)(srcB[q] + k0), (lds_void*)(st + RB_A_BYTES + (q * 4 + wave) * 1024),
+                                       16, 0, 0);
+  };
+
+  f32x16 acc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+  const int sw = rb_swz(lane & 31);
+  const int a_off = (wm * 32 + (lane & 31)) * RB_ROWB;
+
+  if (nk > 0) issue(0);
+  for (int kt = 0; kt < nk; ++kt) {
+    // this wave's loads for step kt are complete; after the barrier everyone's are, and every read of
+    // the stage refilled next (step kt - 1) is done
+    wait_vmcnt<0>();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (kt + 1 < nk) issue(kt + 1);
+    const char* st = lds + (kt & 1) * RB_STAGE;
+#pragma unroll
+    for (int kk = 0; kk < RB_BK / 16; ++kk) {
+      const int coff = ((2 * kk + (lane >> 5)) ^ sw) * 16;
+      const bf16x8 af = *(const bf16x8*)(st + a_off + coff);
+#pragma unroll
+      for (int piece = 2; piece >= 0; --piece)  // smallest piece first
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int brow = piece * RB_BN + wn * 64 + j * 32 + (lane & 31);
+          const bf16x8 bf = *(const bf16x8*)(st + RB_A_BYTES + brow * RB_ROWB + coff);
+          acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc[j], 0, 0, 0);
+        }
+    }
+  }
+  // 32x32 C layout: lane holds column lane % 32, rows 8 (r / 4) + 4 (lane / 32) + r % 4.
+  float* out = part + (int64_t)ks * N * E;
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t n = n0 + wm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      const int e = e0 + wn * 64 + j * 32 + (lane & 31);
+      if (n < N && e < E) out[n * E + e] = acc[j][r];
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// float32 gate GEMM on v_mfma_f32_16x16x4_f32: part[ks, n, e] over the ks-th hidden range.
 // Block tile: 64 tokens x 64 experts, K step 32; 4 waves in 2 x 2, each 32 x 32 (2 x 2 MFMA tiles).
 // LDS holds both tiles k-major with a row pitch of 80 floats: a wave's MFMA operand read touches
 // 4 k-rows x 16 consecutive columns, i.e. 64 distinct banks.
 constexpr int LG_BM = 64, LG_BN = 64, LG_BK = 32, LG_PITCH = 80;
 
 template <typename XT>
-__global__ __launch_bounds__(256) void logits_kernel(const XT* __restrict__ x, const float* __restrict__ wg,
-                                                     float* __restrict__ scores, int64_t N, int D, int E) {
+__global__ __launch_bounds__(256) void logits_f32_kernel(const XT* __restrict__ x, const float* __restrict__ wg,
+                                                         int64_t N, int D, int E, int kchunk,
+                                                         float* __restrict__ part) {
   __shared__ float As[LG_BK][LG_PITCH];
   __shared__ float Bs[LG_BK][LG_PITCH];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t n0 = (int64_t)blockIdx.x * LG_BM;
   const int e0 = blockIdx.y * LG_BN;
+  const int ks = blockIdx.z;
+  const int kbeg = ks * kchunk, kend = min(kbeg + kchunk, D);
 
-  // loader coordinates: 8 consecutive k of one row per thread
   const int lr = t >> 2, lk = (t & 3) * 8;
   const int64_t xrow = n0 + lr;
   const int erow = e0 + lr;
@@ -45,7 +184,7 @@ __global__ __launch_bounds__(256) void logits_kernel(const XT* __restrict__ x, c
   for (int i = 0; i < 2; ++i)
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int k0 = 0; k0 < D; k0 += LG_BK) {
+  for (int k0 = kbeg; k0 < kend; k0 += LG_BK) {
     float av[8], bv[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -74,6 +213,7 @@ __global__ __launch_bounds__(256) void logits_kernel(const XT* __restrict__ x, c
     }
   }
   // C layout of the 16x16 tile: lane holds column lane % 16, rows 4 * (lane / 16) + r.
+  float* out = part + (int64_t)ks * N * E;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -82,25 +222,24 @@ __global__ __launch_bounds__(256) void logits_kernel(const XT* __restrict__ x, c
       for (int r = 0; r < 4; ++r) {
         const int64_t n = n0 + wm * 32 + i * 16 + 4 * (lane >> 4) + r;
         const int e = e0 + wn * 32 + j * 16 + (lane & 15);
-        if (n < N && e < E) {
-          const float logit = acc[i][j][r];
-          scores[n * E + e] = 1.0f / (1.0f + expf(-logit));
-        }
+        if (n < N && e < E) out[n * E + e] = acc[i][j][r];
       }
 }
 
 // ---------------------------------------------------------------------------------------------
 // Selection: one wavefront per token, four tokens per block. Lane l holds experts l, l + 64, ...
-// (up to 8). Every float operation below is one correctly rounded IEEE operation in the order the
-// header states, so given the same scores the result is bit-identical to a plain float32 evaluation.
+// (up to 8). With `part` set, the scores are first formed from the KS logit partials (added in
+// order) and written out; otherwise they are read. Every float operation of the selection is one
+// correctly rounded IEEE operation in the order the header states, so given the same scores the
+// result is bit-identical to a plain float32 evaluation.
 constexpr int SEL_MAX_E = 512, SEL_MAX_P = SEL_MAX_E / 64, SEL_MAX_G = 64, SEL_MAX_K = 32;
 
 __device__ inline bool beats(float av, int ai, float bv, int bi) { return av > bv || (av == bv && ai < bi); }
 
-__global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ scores, const float* __restrict__ bias,
-                                                     int64_t N, int E, int G, int TG, int k, float alpha, int norm,
-                                                     float eps, int32_t* __restrict__ idx_out,
-                                                     float* __restrict__ w_out) {
+__global__ __launch_bounds__(256) void select_kernel(float* __restrict__ scores, const float* __restrict__ part,
+                                                     int KS, const float* __restrict__ bias, int64_t N, int E, int G,
+                                                     int TG, int k, float alpha, int norm, float eps,
+                                                     int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
   __shared__ float s_raw[4][SEL_MAX_E];
   __shared__ float s_sel[4][SEL_MAX_E];
   __shared__ float gscore[4][SEL_MAX_G];
@@ -121,7 +260,14 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ s
     const int e = lane + 64 * p;
     float sv = 0.f, bv = 0.f;
     if (p < P && e < E && live) {
-      sv = scores[n * E + e];
+      if (part) {
+        float r = part[n * E + e];
+        for (int q = 1; q < KS; ++q) r = __fadd_rn(r, part[(int64_t)q * N * E + n * E + e]);
+        sv = 1.0f / (1.0f + expf(-r));  // s = sigmoid(x W_g^T)
+        scores[n * E + e] = sv;
+      } else {
+        sv = scores[n * E + e];
+      }
       bv = bias[e];
     }
     sp[p] = __fadd_rn(sv, bv);  // s' = s + b
@@ -210,22 +356,50 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ s
 
 }  // namespace
 
-hipError_t launch_logits(int dtype, const void* x, const float* wg, const uint16_t* /*wsplit*/, int64_t N, int D,
-                         int E, float* scores, hipStream_t s) {
-  dim3 grid((unsigned)((N + LG_BM - 1) / LG_BM), (unsigned)((E + LG_BN - 1) / LG_BN));
-  if (dtype == MOE_F32)
-    hipLaunchKernelGGL(logits_kernel<float>, grid, dim3(256), 0, s, (const float*)x, wg, scores, N, D, E);
-  else
-    hipLaunchKernelGGL(logits_kernel<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)x, wg, scores, N, D, E);
+RouterPlan router_plan(int dtype, int64_t N, int D, int E) {
+  RouterPlan p;
+  p.split = dtype == MOE_BF16;
+  const int64_t bm = p.split ? RB_BM : LG_BM, bn = p.split ? RB_BN : LG_BN;
+  int64_t tiles = ((N + bm - 1) / bm) * ((E + bn - 1) / bn);
+  if (tiles < 1) tiles = 1;  // N = 0
+  const int64_t want = (512 + tiles - 1) / tiles;  // aim for 512+ blocks
+  const int64_t most = D / 256 > 0 ? D / 256 : 1;  // at least 256 of the hidden dimension per split
+  const int64_t ks = want < 1 ? 1 : (want > most ? most : want);
+  p.kchunk = (int)((D / ks + 31) / 32 * 32);
+  p.ks = (D + p.kchunk - 1) / p.kchunk;
+  return p;
+}
+
+hipError_t launch_router_split(const float* wg, int E, int D, uint16_t* w3, hipStream_t s) {
+  const int64_t count = (int64_t)E * D;
+  int64_t blocks = (count + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(split_kernel, dim3((unsigned)blocks), dim3(256), 0, s, wg, count, w3);
   return hipGetLastError();
 }
 
-hipError_t launch_router_split(const float*, int, int, uint16_t*, hipStream_t) { return hipSuccess; }
+hipError_t launch_logits(int dtype, const RouterPlan& p, const void* x, const float* wg, const uint16_t* w3, int64_t N,
+                         int D, int E, float* part, hipStream_t s) {
+  if (p.split) {
+    dim3 grid((unsigned)((N + RB_BM - 1) / RB_BM), (unsigned)((E + RB_BN - 1) / RB_BN), (unsigned)p.ks);
+    hipLaunchKernelGGL(logits_bf16x3_kernel, grid, dim3(256), 0, s, (const uint16_t*)x, w3, N, D, E, p.kchunk, part);
+  } else {
+    dim3 grid((unsigned)((N + LG_BM - 1) / LG_BM), (unsigned)((E + LG_BN - 1) / LG_BN), (unsigned)p.ks);
+    if (dtype == MOE_F32)
+      hipLaunchKernelGGL(logits_f32_kernel<float>, grid, dim3(256), 0, s, (const float*)x, wg, N, D, E, p.kchunk,
+                         part);
+    else
+      hipLaunchKernelGGL(logits_f32_kernel<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)x, wg, N, D, E,
+                         p.kchunk, part);
+  }
+  return hipGetLastError();
+}
 
-hipError_t launch_select(const float* scores, const float* bias, int64_t N, int E, int G, int TG, int k, float alpha,
-                         int norm, float eps, int32_t* idx, float* w, hipStream_t s) {
+hipError_t launch_select(float* scores, const float* part, int KS, const float* bias, int64_t N, int E, int G, int TG,
+                         int k, float alpha, int norm, float eps, int32_t* idx, float* w, hipStream_t s) {
   dim3 grid((unsigned)((N + 3) / 4));
-  hipLaunchKernelGGL(select_kernel, grid, dim3(256), 0, s, scores, bias, N, E, G, TG, k, alpha, norm, eps, idx, w);
+  hipLaunchKernelGGL(select_kernel, grid, dim3(256), 0, s, scores, part, KS, bias, N, E, G, TG, k, alpha, norm, eps, idx,
+                     w);
   return hipGetLastError();
 }
 

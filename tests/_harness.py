@@ -97,14 +97,16 @@ def gpu_forward(w: synth.Workload, x_dev, dev_w: dict):
 
 
 def score_tolerance(w: synth.Workload, x: np.ndarray, wg: np.ndarray) -> np.ndarray:
-    """Per-element bound on |s_gpu - s_oracle|, from float32 accumulation of D exact products:
-    |dr| <= D u sum_t |x_t W_t| + ulp(r) (u = 2^-24); sigmoid has slope <= 1/4; plus 4 ulp of [0, 1] for
-    the device exp and divide."""
+    """Per-element bound on |s_gpu - s_oracle|. The device logit is a float32 accumulation of at most 3 D
+    exact products (bf16 activations times the three bf16 pieces of the router weight; D products for
+    float32 activations) in partial sums that are then added: |dr| <= 3 D u sum_t |x_t W_t| + ulp(r)
+    (u = 2^-24, the standard recursive-summation bound). The sigmoid has slope <= 1/4; 4 ulp of [0, 1]
+    cover the device exp and divide."""
     xa = np.abs(as_f32(x)).astype(np.float64)
     wa = np.abs(wg).astype(np.float64)
     absdot = xa @ wa.T
     u = 2.0 ** -24
-    return 0.25 * (w.D * u * absdot + absdot * u) + 4 * u
+    return 0.25 * (3 * w.D * u * absdot + absdot * u) + 4 * u
 
 
 def sample_tokens(N: int, count: int, seed: int = 0) -> np.ndarray:

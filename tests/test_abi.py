@@ -36,6 +36,15 @@ def test_workloads_are_supported():
         assert moe.moe_workspace_size(cfg, w.N) > 0
 
 
+def test_workspace_size_small_and_monotone():
+    """Host-only sizing for N = 0, 1 and growing N (no division by an empty tile count)."""
+    for name in synth.WORKLOAD_ORDER:
+        cfg = moe.config_of(synth.WORKLOADS[name])
+        sizes = [moe.moe_workspace_size(cfg, n) for n in (0, 1, 2, 31, 32, 1000)]
+        assert all(a <= b for a, b in zip(sizes, sizes[1:])), (name, sizes)
+    assert moe.moe_workspace_size(cfg, -1) == 0
+
+
 @pytest.mark.parametrize("field,value,status", [
     ("E", 10, moe.MOE_ERR_INVALID_ARG),     # E % G != 0 (G = 4)
     ("G", 16, moe.MOE_ERR_INVALID_ARG),     # groups of one
@@ -68,11 +77,11 @@ def test_argument_errors_before_any_launch():
     w = synth.WORKLOADS["tiny_fp32"]
     cfg = moe.config_of(w)
     L = moe.lib()
-    st = L.moe_route(ctypes.byref(cfg), 4, None, None, None, None, 0, None, None, None)
+    st = L.moe_route(ctypes.byref(cfg), 4, None, None, None, None, 0, None, None, None, 0, None)
     assert st == moe.MOE_ERR_INVALID_ARG
-    st = L.moe_route(ctypes.byref(cfg), -1, None, None, None, None, 0, None, None, None)
+    st = L.moe_route(ctypes.byref(cfg), -1, None, None, None, None, 0, None, None, None, 0, None)
     assert st == moe.MOE_ERR_INVALID_ARG
-    st = L.moe_route(ctypes.byref(cfg), 4, None, None, None, None, 8, None, None, None)  # unknown flag
+    st = L.moe_route(ctypes.byref(cfg), 4, None, None, None, None, 8, None, None, None, 0, None)  # unknown flag
     assert st == moe.MOE_ERR_INVALID_ARG
     ws = moe.MoeWeights()
     st = L.moe_forward(ctypes.byref(cfg), 4, None, ctypes.byref(ws), None, None, None, None, None, 0, None)
@@ -85,7 +94,7 @@ def test_argument_errors_before_any_launch():
     st = L.moe_dispatch(ctypes.byref(cfg), 4, fake, fake, fake, fake, fake, fake, 16, None)
     assert st == moe.MOE_ERR_WORKSPACE
     # N = 0 with nothing else given is a valid no-op for the router and the forward
-    assert L.moe_route(ctypes.byref(cfg), 0, None, None, None, None, 0, None, None, None) == moe.MOE_OK
+    assert L.moe_route(ctypes.byref(cfg), 0, None, None, None, None, 0, None, None, None, 0, None) == moe.MOE_OK
     assert L.moe_forward(ctypes.byref(cfg), 0, None, ctypes.byref(ws), None, None, None, None, None, 0, None) == 0
 
 

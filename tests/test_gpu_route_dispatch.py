@@ -32,7 +32,8 @@ def _route_gpu(w, N, s_host=None, x_host=None, wg=None, b=None):
         moe.moe_route(cfg, N, None, None, b_d, s_d, idx, wt, flags=moe.MOE_ROUTE_SCORES_IN)
     else:
         s_d = torch.empty((N, w.E), dtype=torch.float32, device="cuda")
-        moe.moe_route(cfg, N, H.to_device(x_host), H.to_device(wg), b_d, s_d, idx, wt)
+        moe.moe_route(cfg, N, H.to_device(x_host), H.to_device(wg), b_d, s_d, idx, wt,
+                      workspace=moe.alloc_workspace(cfg, N))
     torch.cuda.synchronize()
     return H.to_host(s_d), H.to_host(idx), H.to_host(wt)
 
