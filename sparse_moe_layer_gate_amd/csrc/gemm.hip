@@ -40,10 +40,10 @@ __device__ inline float silu_mul(float g, float u) { return g / (1.0f + expf(-g)
 // For gate_up a wave's j = 0 / j = 1 tiles are the gate / up projections of 16 intermediate columns.
 template <bool GATE_UP>
 __global__ __launch_bounds__(256) void grouped_f32(GroupedArgs a, int ncol_max) {
-  const int64_t L = xcd_logical_block();
+  const int64_t L = xcd_logical_block((int64_t)*a.n_tiles * ncol_max);
+  if (L < 0) return;
   const int64_t tile_id = L / ncol_max;
   const int ct = (int)(L % ncol_max);
-  if (tile_id >= *a.n_tiles) return;
   const Tile tile = a.tiles[tile_id];
   const ExpertProblem P = pick_problem(a, tile.problem);
   constexpr int COLS = GATE_UP ? F_BN / 2 : F_BN;
@@ -148,16 +148,19 @@ int64_t max_tiles(int64_t N, int k, int E, int n_shared_problem, int bm) {
 
 int gemm_bm(int dtype, int64_t N, int k, int E) {
   if (dtype == MOE_F32) return F_BM;
-  return N * k >= 384LL * E ? 256 : 128;  // 256-row tiles when experts average 384+ rows
+  if (N * k < 48LL * E) return 16;           // weight-streaming decode kernel, 16-row tiles
+  return N * k >= 384LL * E ? 256 : 128;     // 256-row tiles when experts average 384+ rows
 }
 
 hipError_t launch_gate_up(int dtype, const GroupedArgs& a, int64_t max_tile_count, hipStream_t s) {
   if (dtype == MOE_F32) return launch_grouped(grouped_f32<true>, a, max_tile_count, F_BN / 2, s);
+  if (a.bm == 16) return launch_bf16_decode(true, a, max_tile_count, s);
   return launch_bf16_prefill(true, a.bm, a, max_tile_count, s);
 }
 
 hipError_t launch_down(int dtype, const GroupedArgs& a, int64_t max_tile_count, hipStream_t s) {
   if (dtype == MOE_F32) return launch_grouped(grouped_f32<false>, a, max_tile_count, F_BN, s);
+  if (a.bm == 16) return launch_bf16_decode(false, a, max_tile_count, s);
   return launch_bf16_prefill(false, a.bm, a, max_tile_count, s);
 }
 

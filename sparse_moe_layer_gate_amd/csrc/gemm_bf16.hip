@@ -170,12 +170,15 @@ __global__ __launch_bounds__(256, 1) void grouped_bf16_lds(GroupedArgs a, int nc
 
   // Rasterization: logical ids walk GR row tiles down a column before moving right, so the blocks
   // one XCD runs together share GR-fold the B slices and (32 / GR)-fold the A slices.
-  const int64_t L = xcd_logical_block();
+  const int64_t n_tiles = *a.n_tiles;
+  const int64_t L = xcd_logical_block(n_tiles * ncol_max);
+  if (L < 0) return;
   constexpr int GR = MOE_PF_GROUP_ROWS;
   const int64_t sg = L / ((int64_t)GR * ncol_max), within = L % ((int64_t)GR * ncol_max);
-  const int64_t tile_id = sg * GR + within % GR;
-  const int ct = (int)(within / GR);
-  if (tile_id >= *a.n_tiles) return;
+  // the last group may hold fewer than GR row tiles
+  const int64_t gr = min((int64_t)GR, n_tiles - sg * GR);
+  const int64_t tile_id = sg * GR + within % gr;
+  const int ct = (int)(within / gr);
   const Tile tile = a.tiles[tile_id];
   const ExpertProblem P = pick_problem(a, tile.problem);
   const int col0 = ct * T::COLS;

@@ -106,12 +106,17 @@ __device__ inline ExpertProblem pick_problem(const GroupedArgs& a, int p) {
   return r;
 }
 
-// Block id -> logical work id. The hardware deals workgroups to the 8 XCDs round-robin; this remap
-// gives each XCD a contiguous run of logical ids, so the column tiles of one row tile (which share
-// the A rows) and neighbouring row tiles of one expert (which share B) meet in one L2.
-__device__ inline int64_t xcd_logical_block() {
-  const int64_t b = blockIdx.x, nb = gridDim.x;  // nb is a multiple of 8
-  return (b & 7) * (nb >> 3) + (b >> 3);
+// Block id -> logical work id over the nvalid blocks that have work (the grid is sized for the
+// largest possible tile count; the rest return at once). The hardware deals workgroups to the 8 XCDs
+// round-robin (block b to XCD b % 8); this bijection on [0, nvalid) gives each XCD a contiguous run of
+// logical ids of nearly equal length, so the column tiles of one row tile (which share the A rows) and
+// neighbouring row tiles of one expert (which share B) meet in one L2, and all XCDs share the work.
+// Returns -1 for blocks past nvalid.
+__device__ inline int64_t xcd_logical_block(int64_t nvalid) {
+  const int64_t b = blockIdx.x;
+  if (b >= nvalid) return -1;
+  const int64_t x = b & 7, j = b >> 3, q = nvalid >> 3, r = nvalid & 7;
+  return x * q + (x < r ? x : r) + j;
 }
 
 // Upper bound on tiles for a tile list with bm rows per tile.
@@ -120,6 +125,7 @@ int gemm_bm(int dtype, int64_t N, int k, int E);  // rows per tile the forward w
 hipError_t launch_gate_up(int dtype, const GroupedArgs& a, int64_t max_tile_count, hipStream_t s);
 hipError_t launch_down(int dtype, const GroupedArgs& a, int64_t max_tile_count, hipStream_t s);
 hipError_t launch_bf16_prefill(bool gate_up, int bm, const GroupedArgs& a, int64_t max_tile_count, hipStream_t s);
+hipError_t launch_bf16_decode(bool gate_up, const GroupedArgs& a, int64_t max_tile_count, hipStream_t s);
 
 // ---- combine ----
 hipError_t launch_combine(int dtype, const void* Y, const void* Ysh, const int32_t* inv_row, int64_t N, int k, int D,

@@ -363,7 +363,8 @@ RouterPlan router_plan(int dtype, int64_t N, int D, int E) {
   int64_t tiles = ((N + bm - 1) / bm) * ((E + bn - 1) / bn);
   if (tiles < 1) tiles = 1;  // N = 0
   const int64_t want = (512 + tiles - 1) / tiles;  // aim for 512+ blocks
-  const int64_t most = D / 256 > 0 ? D / 256 : 1;  // at least 256 of the hidden dimension per split
+  int64_t most = D / 256 > 0 ? D / 256 : 1;        // at least 256 of the hidden dimension per split
+  if (most > 8) most = 8;                           // and at most 8 partials to add per logit
   const int64_t ks = want < 1 ? 1 : (want > most ? most : want);
   p.kchunk = (int)((D / ks + 31) / 32 * 32);
   p.ks = (D + p.kchunk - 1) / p.kchunk;
