@@ -19,7 +19,6 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -36,7 +35,8 @@ P_F32 = 157.3e12
 HBM = 8.0e12  # B/s
 METRIC = "MoE-layer tokens/s + % bf16 MFMA peak (prefill), % HBM BW (decode)"
 DOMINANT = "experts_gate_up"
-KERNEL_SOURCES = ["sparse_moe_layer_gate_amd/csrc/gemm.hip", "sparse_moe_layer_gate_amd/csrc/moe_internal.h"]
+KERNEL_SOURCES = ["sparse_moe_layer_gate_amd/csrc/gemm_bf16.hip", "sparse_moe_layer_gate_amd/csrc/gemm_decode.hip",
+                  "sparse_moe_layer_gate_amd/csrc/moe_internal.h"]
 
 
 def kernel_source_hash() -> str:
@@ -67,6 +67,81 @@ def read_traffic(workload: str) -> dict | None:
         return None
 
 
+KERNEL_NAMES = {  # library stage -> substring of the HIP kernel symbol
+    "experts_gate_up": ("grouped_bf16_lds<", "true>"),
+    "experts_down": ("grouped_bf16_lds<", "false>"),
+    "experts_gate_up_decode": ("grouped_bf16_decode<true>", ""),
+    "experts_down_decode": ("grouped_bf16_decode<false>", ""),
+}
+
+
+def _csv_rows(path):
+    import csv
+
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _find(dirpath, suffix):
+    for root, _, files in os.walk(dirpath):
+        for fn in files:
+            if fn.endswith(suffix):
+                return os.path.join(root, fn)
+    raise FileNotFoundError(f"no *{suffix} under {dirpath}")
+
+
+def profile_summary(pdir: str, workload: str, decode: bool) -> str:
+    """Markdown summary of a profiling directory laid out as
+         trace/        rocprofv3 --kernel-trace --stats -f csv (this bench, this workload)
+         FETCH_SIZE/   rocprofv3 --pmc FETCH_SIZE -f csv   (this bench, this workload)
+         WRITE_SIZE/   rocprofv3 --pmc WRITE_SIZE -f csv
+         FETCH_SIZE_copy/, WRITE_SIZE_copy/   the same counters on `bench.py --copy-calibration`
+       Byte counters are scaled by bytes-copied / counter-reading of the 1 GiB copy. Also writes the
+       dominant kernel's traffic file read by the benchmark."""
+    stats = _csv_rows(_find(os.path.join(pdir, "trace"), "_kernel_stats.csv"))
+    lines = [f"# rocprofv3 kernel summary: {workload}", "",
+             "| kernel | calls | avg ms | total % |", "|---|---:|---:|---:|"]
+    for r in stats:
+        lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e6:.4f} | "
+                     f"{float(r['Percentage']):.2f} |")
+
+    def per_kernel(sub):
+        rows = _csv_rows(_find(os.path.join(pdir, sub), "_counter_collection.csv"))
+        acc = {}
+        for r in rows:
+            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)  # KiB -> B
+        return {k: sum(v) / len(v) for k, v in acc.items()}
+
+    copy_bytes = float(1 << 30)
+    cf = per_kernel("FETCH_SIZE_copy")
+    cw = per_kernel("WRITE_SIZE_copy")
+    kcopy = next(k for k in cf if "copyBuffer" in k)
+    f_scale = copy_bytes / cf[kcopy]
+    w_scale = copy_bytes / cw[kcopy]
+    fetch, write = per_kernel("FETCH_SIZE"), per_kernel("WRITE_SIZE")
+    lines += ["", "## HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE, calibrated)", "",
+              f"Calibration on a 1 GiB device copy: FETCH_SIZE x {f_scale:.3f}, WRITE_SIZE x {w_scale:.3f}.", "",
+              "| kernel | fetch GB | write GB |", "|---|---:|---:|"]
+    for k in fetch:
+        if k in write:
+            lines.append(f"| `{k[:90]}` | {fetch[k] * f_scale / 1e9:.3f} | {write[k] * w_scale / 1e9:.3f} |")
+    key = KERNEL_NAMES["experts_gate_up_decode" if decode else "experts_gate_up"]
+    dom = [k for k in fetch if key[0] in k and key[1] in k]
+    if dom:
+        k = dom[0]
+        fb, wb = fetch[k] * f_scale, write.get(k, 0.0) * w_scale
+        path = os.path.join(ROOT, "profiles", f"{DOMINANT}_{workload}_traffic.txt")
+        with open(path, "w") as f:
+            f.write(f"# {DOMINANT} on {workload}: HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE,\n"
+                    f"# each scaled by bytes / counter on a 1 GiB device copy (bench.py --copy-calibration).\n"
+                    f"# Commands: see profiles/README.md. Valid while kernel_source_sha matches.\n")
+            f.write(f"kernel: {k}\nkernel_source_sha: {kernel_source_hash()}\n")
+            f.write(f"fetch_scale: {f_scale:.4f}\nwrite_scale: {w_scale:.4f}\n")
+            f.write(f"fetch_bytes_per_launch: {fb:.0f}\nwrite_bytes_per_launch: {wb:.0f}\n")
+            f.write(f"hbm_bytes_per_launch: {fb + wb:.0f}\n")
+    return "\n".join(lines) + "\n"
+
+
 def flops(w: synth.Workload, N: int) -> dict:
     """Algorithmic work of one forward: router (fp32) and the expert GEMMs (bf16)."""
     f32 = 2.0 * N * w.D * w.E
@@ -83,6 +158,42 @@ def algorithmic_bytes(w: synth.Workload, N: int, distinct: int) -> dict:
     act = es * N * w.D * 2  # x in, y out
     gate_up = (distinct + w.n_shared) * 2 * w.d * w.D * es + es * N * w.D  # gate/up weights + x
     return {"layer": weights + router + act, "gate_up": gate_up}
+
+
+def is_decode(w: synth.Workload) -> bool:
+    """Token-poor batches (under 48 rows per expert on average) run the weight-streaming kernels."""
+    return w.N * w.k < 48 * w.E
+
+
+def measure(w: synth.Workload, r: dict) -> dict:
+    """Layer-level rates and the dominant kernel's roofline from one timed run."""
+    distinct = int(np.count_nonzero(r["counts"]))
+    fl = flops(w, w.N)
+    by = algorithmic_bytes(w, w.N, distinct)
+    t_layer = r["ms_per_step"] * 1e-3
+    gu_ms, gu_n = r["stages"][DOMINANT]
+    gu_avg = gu_ms / max(gu_n, 1)
+    traffic = read_traffic(w.name)
+    traffic = None if traffic is None else traffic["bytes"]
+    if is_decode(w):
+        achieved = by["gate_up"] / (gu_avg * 1e-3)
+        roof = {"bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": HBM / 1e9, "unit": "GB/s",
+                "frac": round(achieved / HBM, 4), "traffic": traffic, "kernel": DOMINANT, "avg_ms": round(gu_avg, 4),
+                "per_launch": f"gate/up weights of {distinct} routed + {w.n_shared} shared experts + x = "
+                              f"{by['gate_up'] / 1e9:.4f} GB"}
+    else:
+        achieved = fl["gate_up"] / (gu_avg * 1e-3)
+        roof = {"bound": "mfma", "achieved": round(achieved / 1e12, 2), "peak": P_BF16 / 1e12, "unit": "TFLOP/s",
+                "frac": round(achieved / P_BF16, 4), "traffic": traffic, "kernel": DOMINANT,
+                "avg_ms": round(gu_avg, 4),
+                "per_launch": f"4 D (N k d + N d_sh) = {fl['gate_up'] / 1e12:.4f} TFLOP"}
+    layer = {"tflops": round((fl["bf16"] + fl["router"]) / t_layer / 1e12, 2),
+             "mfma_frac": round(fl["bf16"] / t_layer / P_BF16, 4),
+             "hbm_frac": round(by["layer"] / t_layer / HBM, 4),
+             "algorithmic_bytes": by["layer"],
+             "distinct_experts": distinct, "max_rows_per_expert": int(r["counts"].max()),
+             "stage_ms": {k: round(v[0] / max(v[1], 1), 4) for k, v in r["stages"].items() if v[1]}}
+    return {"ms": r["ms_per_step"], "layer": layer, "roofline": roof}
 
 
 def setup(w: synth.Workload):
@@ -164,7 +275,13 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=2048)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling rocprofv3 byte counters)")
+    ap.add_argument("--profile-summary", metavar="DIR",
+                    help="summarise rocprofv3 output under DIR for --workload (no GPU needed) and exit")
     args = ap.parse_args()
+    if args.profile_summary:
+        w = synth.WORKLOADS[args.workload]
+        print(profile_summary(args.profile_summary, w.name, is_decode(w)), end="")
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
@@ -188,28 +305,15 @@ def main():
     print(f"[bench] {w.name}: generating inputs", file=sys.stderr, flush=True)
     st = setup(w)
     r = time_forward(w, st, args.steps, args.warmup)
-    distinct = int(np.count_nonzero(r["counts"]))
-    fl = flops(w, w.N)
-    by = algorithmic_bytes(w, w.N, distinct)
-    ms = r["ms_per_step"]
-    gu_ms, gu_n = r["stages"][DOMINANT]
-    gu_avg = gu_ms / max(gu_n, 1)
-    achieved = fl["gate_up"] / (gu_avg * 1e-3)
-    traffic = read_traffic(w.name)
-    roof = {"bound": "mfma", "achieved": round(achieved / 1e12, 2), "peak": P_BF16 / 1e12, "unit": "TFLOP/s",
-            "frac": round(achieved / P_BF16, 4), "traffic": None if traffic is None else traffic["bytes"],
-            "kernel": DOMINANT, "avg_ms": round(gu_avg, 4),
-            "per_launch": f"4 D (N k d + N d_sh) = {fl['gate_up'] / 1e12:.4f} TFLOP"}
-    stage_ms = {k: round(v[0] / max(v[1], 1), 4) for k, v in r["stages"].items() if v[1]}
-    t_layer = ms * 1e-3
+    m = measure(w, r)
     out = {
         "metric": METRIC,
-        "value": round(w.N / t_layer, 1),
+        "value": round(w.N / (m["ms"] * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": round(m["ms"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -217,12 +321,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "N": w.N, "D": w.D, "E": w.E, "n_group": w.G, "topk_group": w.TG,
                    "k": w.k, "d_moe": w.d, "n_shared": w.n_shared, "alpha": w.alpha, "parallelism": "none"},
-        "layer": {"tflops": round((fl["bf16"] + fl["router"]) / t_layer / 1e12, 2),
-                  "mfma_frac": round(fl["bf16"] / t_layer / P_BF16, 4),
-                  "hbm_frac": round(by["layer"] / t_layer / HBM, 4),
-                  "distinct_experts": distinct, "max_rows_per_expert": int(r["counts"].max()),
-                  "stage_ms": stage_ms},
-        "roofline": roof,
+        "layer": m["layer"],
+        "roofline": m["roofline"],
     }
     del st
     torch.cuda.empty_cache()
@@ -231,23 +331,9 @@ def main():
         wd = synth.WORKLOADS["glm5_decode"]
         print(f"[bench] {wd.name}: generating inputs", file=sys.stderr, flush=True)
         sd = setup(wd)
-        rd = time_forward(wd, sd, args.decode_steps, args.warmup)
-        dd = int(np.count_nonzero(rd["counts"]))
-        byd = algorithmic_bytes(wd, wd.N, dd)
-        msd = rd["ms_per_step"]
-        gms, gn = rd["stages"][DOMINANT]
-        g_avg = gms / max(gn, 1)
-        out["decode"] = {
-            "workload": wd.name, "tokens_per_s": round(wd.N / (msd * 1e-3), 1), "ms_per_step": round(msd, 4),
-            "distinct_experts": dd,
-            "hbm_frac": round(byd["layer"] / (msd * 1e-3) / HBM, 4),
-            "algorithmic_bytes": byd["layer"],
-            "roofline": {"bound": "hbm", "achieved": round(byd["gate_up"] / (g_avg * 1e-3) / 1e9, 1),
-                         "peak": HBM / 1e9, "unit": "GB/s",
-                         "frac": round(byd["gate_up"] / (g_avg * 1e-3) / HBM, 4), "traffic": None,
-                         "kernel": DOMINANT, "avg_ms": round(g_avg, 4)},
-            "stage_ms": {k: round(v[0] / max(v[1], 1), 4) for k, v in rd["stages"].items() if v[1]},
-        }
+        md = measure(wd, time_forward(wd, sd, args.decode_steps, args.warmup))
+        out["decode"] = {"workload": wd.name, "tokens_per_s": round(wd.N / (md["ms"] * 1e-3), 1),
+                         "ms_per_step": round(md["ms"], 4), "layer": md["layer"], "roofline": md["roofline"]}
         del sd
         torch.cuda.empty_cache()
 
