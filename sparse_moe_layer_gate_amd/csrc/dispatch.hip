@@ -3,7 +3,7 @@
 //   count: per chunk of tokens, an LDS histogram of expert ids;
 //   scan : per expert, an exclusive scan over chunks, then an exclusive scan over experts (offsets),
 //          and the row-tile lists the grouped GEMMs walk;
-//   place: per chunk, each expert's pairs written in token order from that chunk's base.
+//   place: per chunk, each pair written at its expert's chunk base + its stable rank in the chunk.
 // The result is the stable order: tokens ascending inside each expert.
 #include <hip/hip_runtime.h>
 
@@ -42,88 +42,122 @@ __device__ void write_tiles(const TileSpec& ts, int e, int count, int offset, in
   }
 }
 
+// Exclusive scan of one int per thread over a 512-thread block (8 waves): shuffles inside each wave,
+// then the wave totals. Returns the exclusive prefix; *total receives the block sum.
+__device__ int block_exclusive_scan(int v, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int w = 0; w < 8; ++w) {
+    const int t = wsum[w];
+    before += w < wave ? t : 0;
+    all += t;
+  }
+  __syncthreads();  // wsum is reused by the next scan
+  *total = all;
+  return before + incl - v;
+}
+
+__device__ void write_shared_tiles(const TileSpec& ts, int routed_tiles, int64_t N, int n_shared_problem) {
+  const int64_t nsh = n_shared_problem ? (N + ts.bm - 1) / ts.bm : 0;
+  for (int64_t j = threadIdx.x; j < nsh; j += blockDim.x) {
+    Tile t;
+    t.problem = 1;
+    t.expert = 0;
+    t.row_start = (int)(j * ts.bm);
+    t.rows = (int)min((int64_t)ts.bm, N - j * ts.bm);
+    ts.tiles[routed_tiles + j] = t;
+  }
+  if (threadIdx.x == 0) *ts.n_tiles = routed_tiles + (int)nsh;
+}
+
 __global__ __launch_bounds__(512) void scan_kernel(const int32_t* __restrict__ chunk_counts, int nchunks, int64_t N,
                                                    int k, int E, int n_shared_problem, int32_t* __restrict__ counts,
                                                    int32_t* __restrict__ offsets, int32_t* __restrict__ chunk_base,
                                                    TileSpec t0, TileSpec t1) {
-  __shared__ int cnt[MAX_E];
-  __shared__ int off[MAX_E + 1];
-  __shared__ int toff0[MAX_E + 1];
-  __shared__ int toff1[MAX_E + 1];
+  __shared__ int wsum[8];
   const int e = threadIdx.x;
-  int total = 0;
+  // per expert: exclusive scan over chunks (chunk bases before the expert offset is known)
+  int cnt = 0;
   if (e < E) {
     for (int c = 0; c < nchunks; ++c) {
       const int v = chunk_counts[(int64_t)c * E + e];
-      chunk_base[(int64_t)c * E + e] = total;
-      total += v;
+      chunk_base[(int64_t)c * E + e] = cnt;
+      cnt += v;
     }
-    cnt[e] = total;
   }
-  __syncthreads();
-  if (e == 0) {  // exclusive scans over experts (E <= 512: a short serial loop)
-    int run = 0, r0 = 0, r1 = 0;
-    for (int i = 0; i < E; ++i) {
-      off[i] = run;
-      toff0[i] = r0;
-      toff1[i] = r1;
-      run += cnt[i];
-      r0 += (cnt[i] + t0.bm - 1) / t0.bm;
-      r1 += (cnt[i] + t1.bm - 1) / t1.bm;
-    }
-    off[E] = run;
-    toff0[E] = r0;
-    toff1[E] = r1;
-  }
-  __syncthreads();
+  const int nt0 = e < E ? (cnt + t0.bm - 1) / t0.bm : 0;
+  const int nt1 = e < E ? (cnt + t1.bm - 1) / t1.bm : 0;
+  int total, tiles0, tiles1;
+  const int off = block_exclusive_scan(cnt, wsum, &total);
+  const int toff0 = block_exclusive_scan(nt0, wsum, &tiles0);
+  const int toff1 = block_exclusive_scan(nt1, wsum, &tiles1);
   if (e < E) {
-    counts[e] = cnt[e];
-    offsets[e] = off[e];
-    for (int c = 0; c < nchunks; ++c) chunk_base[(int64_t)c * E + e] += off[e];
-    write_tiles(t0, e, cnt[e], off[e], toff0[e]);
-    write_tiles(t1, e, cnt[e], off[e], toff1[e]);
+    counts[e] = cnt;
+    offsets[e] = off;
+    for (int c = 0; c < nchunks; ++c) chunk_base[(int64_t)c * E + e] += off;
+    write_tiles(t0, e, cnt, off, toff0);
+    write_tiles(t1, e, cnt, off, toff1);
   }
-  if (e == 0) offsets[E] = off[E];
+  if (e == 0) offsets[E] = total;
   // the shared expert's tiles follow the routed ones: all N tokens, in token order
-  const TileSpec* specs[2] = {&t0, &t1};
-  const int routed_tiles[2] = {toff0[E], toff1[E]};
-  for (int sidx = 0; sidx < 2; ++sidx) {
-    const TileSpec& ts = *specs[sidx];
-    const int64_t nsh = n_shared_problem ? (N + ts.bm - 1) / ts.bm : 0;
-    for (int64_t j = threadIdx.x; j < nsh; j += blockDim.x) {
-      Tile t;
-      t.problem = 1;
-      t.expert = 0;
-      t.row_start = (int)(j * ts.bm);
-      t.rows = (int)min((int64_t)ts.bm, N - j * ts.bm);
-      ts.tiles[routed_tiles[sidx] + j] = t;
-    }
-    if (threadIdx.x == 0) *ts.n_tiles = routed_tiles[sidx] + (int)nsh;
-  }
+  write_shared_tiles(t0, tiles0, N, n_shared_problem);
+  write_shared_tiles(t1, tiles1, N, n_shared_problem);
 }
 
+// Stable placement of one chunk: rounds of 256 pairs (in pair order); inside a round, a pair's
+// position is its expert's running offset + the pairs of that expert in earlier waves of the round +
+// those in earlier lanes of its own wave (found with 64 shuffles). Tokens stay ascending inside each
+// expert because pairs are visited in (token, slot) order.
 __global__ __launch_bounds__(256) void place_kernel(const int32_t* __restrict__ idx, int64_t N, int k, int E,
                                                     const int32_t* __restrict__ chunk_base,
                                                     int32_t* __restrict__ sorted_pair, int32_t* __restrict__ inv_row) {
-  extern __shared__ int lidx[];  // CH * k ids of this chunk
-  const int c = blockIdx.x;
+  __shared__ int running[MAX_E];
+  __shared__ int wcnt[4][MAX_E];
+  const int c = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int64_t first = (int64_t)c * CH * k;
   const int npairs = (int)(min((int64_t)(c + 1) * CH, N) * k - first);
-  for (int p = threadIdx.x; p < npairs; p += 256) {
-    const int e = idx[first + p];
-    lidx[p] = e;
-    if (e < 0 || e >= E) inv_row[first + p] = -1;
+  for (int e = t; e < E; e += 256) {
+    running[e] = chunk_base[(int64_t)c * E + e];
+    for (int w = 0; w < 4; ++w) wcnt[w][e] = 0;
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 256) {
-    int cur = chunk_base[(int64_t)c * E + e];
-    for (int p = 0; p < npairs; ++p) {
-      if (lidx[p] == e) {
-        sorted_pair[cur] = (int32_t)(first + p);
-        inv_row[first + p] = cur;
-        ++cur;
+  for (int r0 = 0; r0 < npairs; r0 += 256) {
+    const int p = r0 + t;
+    int e = -1;
+    if (p < npairs) {
+      e = idx[first + p];
+      if (e < 0 || e >= E) {
+        e = -1;
+        inv_row[first + p] = -1;
       }
     }
+    int rank = 0;
+    for (int j = 0; j < 64; ++j) {
+      const int ej = __shfl(e, j);
+      rank += (j < lane && ej == e) ? 1 : 0;
+    }
+    if (e >= 0) atomicAdd(&wcnt[wave][e], 1);
+    __syncthreads();
+    if (e >= 0) {
+      int pos = running[e] + rank;
+      for (int w = 0; w < wave; ++w) pos += wcnt[w][e];
+      sorted_pair[pos] = (int32_t)(first + p);
+      inv_row[first + p] = pos;
+    }
+    __syncthreads();
+    for (int e2 = t; e2 < E; e2 += 256) {
+      running[e2] += wcnt[0][e2] + wcnt[1][e2] + wcnt[2][e2] + wcnt[3][e2];
+      for (int w = 0; w < 4; ++w) wcnt[w][e2] = 0;
+    }
+    __syncthreads();
   }
 }
 
@@ -146,8 +180,7 @@ hipError_t launch_scan(const int32_t* chunk_counts, int nchunks, int64_t N, int 
 hipError_t launch_place(const int32_t* idx, int64_t N, int k, int E, const int32_t* chunk_base, int32_t* sorted_pair,
                         int32_t* inv_row, hipStream_t s) {
   const int nchunks = (int)((N + CH - 1) / CH);
-  const size_t lds = (size_t)CH * k * sizeof(int);
-  hipLaunchKernelGGL(place_kernel, dim3(nchunks), dim3(256), lds, s, idx, N, k, E, chunk_base, sorted_pair, inv_row);
+  hipLaunchKernelGGL(place_kernel, dim3(nchunks), dim3(256), 0, s, idx, N, k, E, chunk_base, sorted_pair, inv_row);
   return hipGetLastError();
 }
 

@@ -74,7 +74,9 @@ struct PrefillTile {
     const int k0 = kstep * BK;
 #pragma unroll
     for (int q = 0; q < NA; ++q)
-      __builtin_amdgcn_global_load_lds((const void*)(srcA[q] + k0), (lds_void*)(st + (q * 4 + wave) * 1024), 16, 0, 0);
+      if (srcA[q])  // rows past the tile's valid rows are not loaded (their MFMA outputs are not stored)
+        __builtin_amdgcn_global_load_lds((const void*)(srcA[q] + k0), (lds_void*)(st + (q * 4 + wave) * 1024), 16, 0,
+                                         0);
 #pragma unroll
     for (int q = 0; q < NB; ++q)
       __builtin_amdgcn_global_load_lds((const void*)(srcB[q] + k0), (lds_void*)(st + BM * ROWB + (q * 4 + wave) * 1024),
@@ -165,7 +167,9 @@ __global__ __launch_bounds__(256, 1) void grouped_bf16_lds(GroupedArgs a, int nc
   constexpr int BN = T::BN, CPR = T::CPR, NA = T::NA, NB = T::NB, TM = T::TM, TN = T::TN;
   constexpr int WAVE_M = T::WAVE_M, WAVE_N = T::WAVE_N;
 
-  __shared__ __attribute__((aligned(1024))) char lds[STAGES * T::STAGE_BYTES];
+  constexpr int OUT_BYTES = 4 * WAVE_M * ((GATE_UP ? WAVE_N / 2 : WAVE_N) + 8) * 2;
+  constexpr int LDS_BYTES = STAGES * T::STAGE_BYTES > OUT_BYTES ? STAGES * T::STAGE_BYTES : OUT_BYTES;
+  __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
   __shared__ float wrow[BM];
 
   // Rasterization: logical ids walk GR row tiles down a column before moving right, so the blocks
@@ -198,6 +202,9 @@ __global__ __launch_bounds__(256, 1) void grouped_bf16_lds(GroupedArgs a, int nc
     int64_t g = (int64_t)tile.row_start + min(r, tile.rows - 1);
     if (P.gather) g = a.sorted_pair[g] / a.k;
     srcA[q] = (const uint16_t*)P.A + g * P.lda + 8 * c;
+    // Skipping a load leaves fewer VMEM ops in flight than the vmcnt thresholds of a deeper ring
+    // assume, so only the two-stage ring (which waits for all of them) skips.
+    if (STAGES == 2 && r >= tile.rows) srcA[q] = nullptr;
   }
 #pragma unroll
   for (int q = 0; q < NB; ++q) {
@@ -240,30 +247,43 @@ __global__ __launch_bounds__(256, 1) void grouped_bf16_lds(GroupedArgs a, int nc
   }
 #undef MOE_PF_RUN
 
+  // Epilogue through LDS: each wave writes its bf16 results (SwiGLU / weight scale applied) into its
+  // own padded region, then stores whole 16-byte row chunks, so a store instruction covers
+  // contiguous runs of the output rows instead of 2-byte scatters.
+  constexpr int OC = GATE_UP ? WAVE_N / 2 : WAVE_N;  // output columns per wave
+  constexpr int OPITCH = OC + 8;                      // bf16 per staged row (16-byte pad: the two
+                                                      // half-waves' rows land on disjoint banks)
+  __syncthreads();  // every wave is done reading the operand ring
+  uint16_t* stage_out = (uint16_t*)lds + wave * (WAVE_M * OPITCH);
   // 32x32 C layout: lane holds column lane % 32, rows 8 (r / 4) + 4 (lane / 32) + r % 4.
-  uint16_t* out = (uint16_t*)P.out;
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     if (i >= mi) continue;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int row = wm * WAVE_M + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      if (row >= tile.rows) continue;
-      const int64_t orow = (int64_t)tile.row_start + row;
+      const int row = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);  // within the wave slab
       if (GATE_UP) {
 #pragma unroll
-        for (int j = 0; j < TN / 2; ++j) {
-          const int col = col0 + wn * (WAVE_N / 2) + j * 32 + (lane & 31);
-          if (col < P.ncols) out[orow * P.ldo + col] = bf16_rne(silu_mul(acc[i][j][r], acc[i][j + TN / 2][r]));
-        }
+        for (int j = 0; j < TN / 2; ++j)
+          stage_out[row * OPITCH + j * 32 + (lane & 31)] = bf16_rne(silu_mul(acc[i][j][r], acc[i][j + TN / 2][r]));
       } else {
-        const float sc = wrow[row];
+        const float sc = wrow[min(wm * WAVE_M + row, BM - 1)];
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int col = col0 + wn * WAVE_N + j * 32 + (lane & 31);
-          if (col < P.ncols) out[orow * P.ldo + col] = bf16_rne(acc[i][j][r] * sc);
-        }
+        for (int j = 0; j < TN; ++j) stage_out[row * OPITCH + j * 32 + (lane & 31)] = bf16_rne(acc[i][j][r] * sc);
       }
+    }
+  }
+  __syncthreads();
+  uint16_t* out = (uint16_t*)P.out;
+  const int ocol0 = col0 + wn * OC;
+  constexpr int CH = OC / 8;  // 16-byte chunks per staged row
+  const int rows_here = min(WAVE_M, tile.rows - wm * WAVE_M);
+  for (int c = lane; c < rows_here * CH; c += 64) {
+    const int row = c / CH, ch = c % CH;
+    const int col = ocol0 + ch * 8;
+    if (col < P.ncols) {  // ncols is a multiple of 64: a chunk is wholly in or out
+      const uint4 v = *(const uint4*)(stage_out + row * OPITCH + ch * 8);
+      *(uint4*)(out + ((int64_t)tile.row_start + wm * WAVE_M + row) * P.ldo + col) = v;
     }
   }
 }

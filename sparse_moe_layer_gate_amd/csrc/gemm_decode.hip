@@ -19,7 +19,14 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int DC_U = 4;  // K-slices of 32 per loop iteration
+#ifndef MOE_DC_U
+#define MOE_DC_U 8
+#endif
+#ifndef MOE_DC_NT
+#define MOE_DC_NT 2
+#endif
+constexpr int DC_U = MOE_DC_U;    // K-slices of 32 per loop iteration
+constexpr int DC_NT = MOE_DC_NT;  // 16-column MFMA tiles per wave (gate_up: half gate, half up)
 
 __device__ inline uint16_t bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -31,9 +38,10 @@ __device__ inline float silu_mul(float g, float u) { return g / (1.0f + expf(-g)
 
 template <bool GATE_UP>
 __global__ __launch_bounds__(256) void grouped_bf16_decode(GroupedArgs a, int ncol_max) {
-  constexpr int WAVE_COLS = GATE_UP ? 32 : 64;  // output columns per wave
+  constexpr int NT = DC_NT;
+  constexpr int WAVE_COLS = GATE_UP ? NT / 2 * 16 : NT * 16;  // output columns per wave
   constexpr int BLOCK_COLS = 4 * WAVE_COLS;
-  constexpr int NT = 4;  // 16-column MFMA tiles per wave (gate_up: gate 0, gate 1, up 0, up 1)
+  static_assert(NT % 2 == 0, "gate_up pairs gate and up tiles");
 
   const int64_t L = xcd_logical_block((int64_t)*a.n_tiles * ncol_max);
   if (L < 0) return;
@@ -61,8 +69,8 @@ __global__ __launch_bounds__(256) void grouped_bf16_decode(GroupedArgs a, int nc
     const uint16_t* base;
     int col;
     if (GATE_UP) {
-      base = (const uint16_t*)(j < 2 ? P.B0 : P.B1);
-      col = wcol0 + (j & 1) * 16 + r16;
+      base = (const uint16_t*)(j < NT / 2 ? P.B0 : P.B1);
+      col = wcol0 + (j % (NT / 2)) * 16 + r16;
     } else {
       base = (const uint16_t*)P.B0;
       col = wcol0 + j * 16 + r16;
@@ -108,9 +116,9 @@ __global__ __launch_bounds__(256) void grouped_bf16_decode(GroupedArgs a, int nc
     const int64_t orow = (int64_t)tile.row_start + row;
     if (GATE_UP) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < NT / 2; ++j) {
         const int col = wcol0 + j * 16 + r16;
-        if (col < P.ncols) out[orow * P.ldo + col] = bf16_rne(silu_mul(acc[j][i], acc[j + 2][i]));
+        if (col < P.ncols) out[orow * P.ldo + col] = bf16_rne(silu_mul(acc[j][i], acc[j + NT / 2][i]));
       }
     } else {
       const float sc = P.scale_rows ? a.topk_w[a.sorted_pair[orow]] : 1.0f;
@@ -125,7 +133,7 @@ __global__ __launch_bounds__(256) void grouped_bf16_decode(GroupedArgs a, int nc
 
 template <bool GATE_UP>
 hipError_t launch(const GroupedArgs& a, int64_t max_tile_count, hipStream_t s) {
-  constexpr int BLOCK_COLS = GATE_UP ? 128 : 256;
+  constexpr int BLOCK_COLS = 4 * (GATE_UP ? DC_NT / 2 * 16 : DC_NT * 16);
   int nc = 0;
   for (int p = 0; p < 2; ++p)
     if (a.prob[p].out) nc = max(nc, (a.prob[p].ncols + BLOCK_COLS - 1) / BLOCK_COLS);

@@ -233,6 +233,7 @@ __global__ __launch_bounds__(256) void logits_f32_kernel(const XT* __restrict__ 
 // correctly rounded IEEE operation in the order the header states, so given the same scores the
 // result is bit-identical to a plain float32 evaluation.
 constexpr int SEL_MAX_E = 512, SEL_MAX_P = SEL_MAX_E / 64, SEL_MAX_G = 64, SEL_MAX_K = 32;
+constexpr int SEL_MAX_KS = 16;  // logit partials per score (router_plan keeps KS within this)
 
 __device__ inline bool beats(float av, int ai, float bv, int bi) { return av > bv || (av == bv && ai < bi); }
 
@@ -261,8 +262,14 @@ __global__ __launch_bounds__(256) void select_kernel(float* __restrict__ scores,
     float sv = 0.f, bv = 0.f;
     if (p < P && e < E && live) {
       if (part) {
-        float r = part[n * E + e];
-        for (int q = 1; q < KS; ++q) r = __fadd_rn(r, part[(int64_t)q * N * E + n * E + e]);
+        // all KS partials are loaded before the first add, then added in order
+        float pv[SEL_MAX_KS];
+#pragma unroll
+        for (int q = 0; q < SEL_MAX_KS; ++q) pv[q] = q < KS ? part[(int64_t)q * N * E + n * E + e] : 0.f;
+        float r = pv[0];
+#pragma unroll
+        for (int q = 1; q < SEL_MAX_KS; ++q)
+          if (q < KS) r = __fadd_rn(r, pv[q]);
         sv = 1.0f / (1.0f + expf(-r));  // s = sigmoid(x W_g^T)
         scores[n * E + e] = sv;
       } else {
@@ -364,7 +371,7 @@ RouterPlan router_plan(int dtype, int64_t N, int D, int E) {
   if (tiles < 1) tiles = 1;  // N = 0
   const int64_t want = (512 + tiles - 1) / tiles;  // aim for 512+ blocks
   int64_t most = D / 256 > 0 ? D / 256 : 1;        // at least 256 of the hidden dimension per split
-  if (most > 8) most = 8;                           // and at most 8 partials to add per logit
+  if (most > 16) most = 16;                         // and at most 16 partials to add per logit
   const int64_t ks = want < 1 ? 1 : (want > most ? most : want);
   p.kchunk = (int)((D / ks + 31) / 32 * 32);
   p.ks = (D + p.kchunk - 1) / p.kchunk;
