@@ -20,7 +20,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 #ifndef MOE_DC_U
-#define MOE_DC_U 8
+#define MOE_DC_U 16
 #endif
 #ifndef MOE_DC_NT
 #define MOE_DC_NT 2
