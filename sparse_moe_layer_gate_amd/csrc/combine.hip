@@ -25,11 +25,6 @@ __device__ inline void add8(float* acc, const float* p) {
   acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
   acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
 }
-__device__ inline uint16_t bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
 __device__ inline void store8(uint16_t* p, const float* acc) {
   uint4 v;
   v.x = (uint32_t)bf16_rne(acc[0]) | ((uint32_t)bf16_rne(acc[1]) << 16);

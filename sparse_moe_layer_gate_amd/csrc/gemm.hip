@@ -27,14 +27,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int F_BM = 64, F_BN = 64;                      // fp32 path
 
-__device__ inline uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
-__device__ inline float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
-
 // fp32 layers: 64 x 64 block tile, 4 waves in 2 x 2, each 32 x 32 as 2 x 2 tiles of
 // v_mfma_f32_16x16x4_f32 (A: row lane % 16, k lane / 16; C: column lane % 16, rows 4 (lane / 16) + r).
 // For gate_up a wave's j = 0 / j = 1 tiles are the gate / up projections of 16 intermediate columns.

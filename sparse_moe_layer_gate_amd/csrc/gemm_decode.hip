@@ -2,13 +2,16 @@
 //
 // With one or two tokens per expert the layer is a weight stream ("Module 02 -- MoE: Capacity, Work,
 // and Traffic", section 1: traffic, not arithmetic, governs decode), so this kernel is built to keep
-// as many weight bytes in flight as possible and to touch each weight byte once:
+// many weight bytes in flight and to move each weight byte once, in whole cache lines:
 //  - row tiles of at most 16 rows (the tile list is built with 16 rows per tile);
-//  - no LDS and no barriers: each wave streams its own weight rows (16 output columns per
-//    v_mfma_f32_16x16x32_bf16 tile) straight from HBM into registers, U K-slices per iteration, and
-//    reads the few activation rows from L2; many independent waves per CU hide the HBM latency;
-//  - gate_up: each wave owns 32 intermediate columns as two gate and two up tiles and applies the
-//    SwiGLU in registers; down: each wave owns 64 output columns and scales each row by its weight.
+//  - each wave owns NT 16-column tiles of one expert (gate_up: NT/2 gate and NT/2 up tiles, SwiGLU in
+//    registers; down: NT tiles, each row scaled by its weight) and works alone: no block barriers;
+//  - loaded straight into registers, the MFMA operand layout (v_mfma_f32_16x16x32_bf16: a lane holds
+//    8 k of one row) makes every load touch 16 rows x 64 bytes, half of each 128-byte line, which
+//    costs about a fifth of the stream rate. Instead each wave copies its rows into a private LDS ring
+//    with global_load_lds_dwordx4, CPR 16-byte chunks per row and stage (whole lines), S stages deep,
+//    and reads them back in MFMA layout. The ring also holds the wave's activation rows, so every
+//    stage is the same fixed number of DMA instructions and one vmcnt wait orders the ring.
 #include <hip/hip_runtime.h>
 
 #include "moe_internal.h"
@@ -20,28 +23,45 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 #ifndef MOE_DC_U
-#define MOE_DC_U 16
+#define MOE_DC_U 4
+#endif
+#ifndef MOE_DC_S
+#define MOE_DC_S 2
 #endif
 #ifndef MOE_DC_NT
 #define MOE_DC_NT 2
 #endif
-constexpr int DC_U = MOE_DC_U;    // K-slices of 32 per loop iteration
-constexpr int DC_NT = MOE_DC_NT;  // 16-column MFMA tiles per wave (gate_up: half gate, half up)
 
-__device__ inline uint16_t bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
+template <bool GATE_UP>
+struct DecodeTile {
+  static constexpr int NT = MOE_DC_NT;  // 16-column weight tiles per wave
+  static constexpr int U = MOE_DC_U;    // 32-wide K slices per stage
+  static constexpr int S = MOE_DC_S;    // ring depth (stages)
+  static constexpr int SK = 32 * U;     // K elements per stage
+  static constexpr int CPR = SK / 8;    // 16-byte chunks per row and stage
+  static constexpr int RPI = 64 / CPR;  // rows per DMA instruction
+  static constexpr int QPT = 16 / RPI;  // DMA instructions per 16-row tile and stage
+  static constexpr int TILE_BYTES = 16 * SK * 2;
+  static constexpr int STAGE_BYTES = (NT + 1) * TILE_BYTES;  // activation tile, then NT weight tiles
+  static constexpr int WAVE_BYTES = S * STAGE_BYTES;
+  static constexpr int NDMA = (NT + 1) * QPT;  // DMA instructions per stage
+  static constexpr int WAVE_COLS = GATE_UP ? NT / 2 * 16 : NT * 16;  // output columns per wave
+  static constexpr int BLOCK_COLS = 4 * WAVE_COLS;
+  static_assert(!GATE_UP || NT % 2 == 0, "gate_up pairs gate and up tiles");
+  static_assert(CPR >= 8 && CPR <= 64 && 64 % CPR == 0, "a DMA instruction covers whole 128-byte lines");
+  static_assert((S - 1) * NDMA < 64, "vmcnt is 6 bits");
+  static_assert(4 * WAVE_BYTES <= 160 * 1024, "LDS per CU");
 
-__device__ inline float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+  // Chunk swizzle: chunk c of row r sits in slot c ^ sig(r). For each MFMA operand read (16 lanes of
+  // one k group over rows 0..15) the 16 slots then fall in distinct 16-byte bank groups.
+  __device__ static int sig(int r) { return CPR >= 16 ? r : r / (16 / CPR); }
+};
 
 template <bool GATE_UP>
 __global__ __launch_bounds__(256) void grouped_bf16_decode(GroupedArgs a, int ncol_max) {
-  constexpr int NT = DC_NT;
-  constexpr int WAVE_COLS = GATE_UP ? NT / 2 * 16 : NT * 16;  // output columns per wave
-  constexpr int BLOCK_COLS = 4 * WAVE_COLS;
-  static_assert(NT % 2 == 0, "gate_up pairs gate and up tiles");
+  using T = DecodeTile<GATE_UP>;
+  constexpr int NT = T::NT, U = T::U, S = T::S, SK = T::SK, CPR = T::CPR, RPI = T::RPI, QPT = T::QPT;
+  __shared__ __attribute__((aligned(1024))) char lds[4 * T::WAVE_BYTES];
 
   const int64_t L = xcd_logical_block((int64_t)*a.n_tiles * ncol_max);
   if (L < 0) return;
@@ -49,62 +69,92 @@ __global__ __launch_bounds__(256) void grouped_bf16_decode(GroupedArgs a, int nc
   const int ct = (int)(L % ncol_max);
   const Tile tile = a.tiles[tile_id];
   const ExpertProblem P = pick_problem(a, tile.problem);
-  const int col0 = ct * BLOCK_COLS;
+  const int col0 = ct * T::BLOCK_COLS;
   if (col0 >= P.ncols) return;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wcol0 = col0 + wave * WAVE_COLS;
-  const int r16 = lane & 15, kq = lane >> 4;  // operand row / column within a tile, 8-element k group
+  const int wcol0 = col0 + wave * T::WAVE_COLS;
+  char* const ring = lds + wave * T::WAVE_BYTES;
 
-  // activation row of this lane (A operand: row r16, k 8 kq .. 8 kq + 7 of each 32-slice)
-  const bool arow_ok = r16 < tile.rows;
-  int64_t g = (int64_t)tile.row_start + min(r16, tile.rows - 1);
-  if (P.gather) g = a.sorted_pair[g] / a.k;
-  const uint16_t* aptr = (const uint16_t*)P.A + g * P.lda + 8 * kq;
-
-  // weight rows (B operand: output column r16 of each 16-column tile)
-  const uint16_t* bptr[NT];
+  // DMA sources of this lane: in instruction q of a tile it moves chunk chunk[q] of tile row
+  // q * RPI + lane / CPR into slot lane % CPR of that row. Every lane of every instruction is active:
+  // activation rows past tile.rows repeat the last valid row and weight rows past ncols repeat the
+  // last column (neither reaches a stored output), so each stage is exactly NDMA instructions.
+  const uint16_t* src[NT + 1][QPT];
+  int chunk[QPT];
 #pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    const uint16_t* base;
-    int col;
-    if (GATE_UP) {
-      base = (const uint16_t*)(j < NT / 2 ? P.B0 : P.B1);
-      col = wcol0 + (j % (NT / 2)) * 16 + r16;
-    } else {
-      base = (const uint16_t*)P.B0;
-      col = wcol0 + j * 16 + r16;
+  for (int q = 0; q < QPT; ++q) {
+    const int r = q * RPI + lane / CPR;
+    chunk[q] = (lane % CPR) ^ T::sig(r);
+    int64_t g = (int64_t)tile.row_start + min(r, tile.rows - 1);
+    if (P.gather) g = a.sorted_pair[g] / a.k;
+    src[0][q] = (const uint16_t*)P.A + g * P.lda;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const uint16_t* base;
+      int col;
+      if (GATE_UP) {
+        base = (const uint16_t*)(j < NT / 2 ? P.B0 : P.B1);
+        col = wcol0 + (j % (NT / 2)) * 16 + r;
+      } else {
+        base = (const uint16_t*)P.B0;
+        col = wcol0 + j * 16 + r;
+      }
+      col = min(col, P.ncols - 1);
+      src[1 + j][q] = base + (int64_t)tile.expert * P.b_stride + (int64_t)col * P.K;
     }
-    col = min(col, P.ncols - 1);
-    bptr[j] = base + (int64_t)tile.expert * P.b_stride + (int64_t)col * P.K + 8 * kq;
   }
 
+  const int nst = (P.K + SK - 1) / SK;
+  const int ktail = P.K - (nst - 1) * SK;  // K elements of the last stage (a multiple of 32)
+
+  // Stage t -> ring slot t % S. In a short last stage, chunks past K load the last chunk in K instead
+  // (their slots are never read), keeping every address inside its row.
+  auto issue = [&](int t) {
+    char* st = ring + (t % S) * T::STAGE_BYTES;
+    const int kmax = t == nst - 1 ? ktail : SK;
+#pragma unroll
+    for (int q = 0; q < QPT; ++q) {
+      const int64_t ke = (int64_t)t * SK + 8 * min(chunk[q], kmax / 8 - 1);
+#pragma unroll
+      for (int j = 0; j <= NT; ++j)
+        __builtin_amdgcn_global_load_lds((const void*)(src[j][q] + ke), (lds_void*)(st + j * T::TILE_BYTES + q * 1024),
+                                         16, 0, 0);
+    }
+  };
+
+  const int r16 = lane & 15, kq = lane >> 4;  // MFMA operand row and 8-element k group of this lane
   f32x4 acc[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const bf16x8 zero8 = {};
-  int k0 = 0;
-  for (; k0 + 32 * DC_U <= P.K; k0 += 32 * DC_U) {
-    bf16x8 av[DC_U], bv[DC_U][NT];
 #pragma unroll
-    for (int u = 0; u < DC_U; ++u) {
-#pragma unroll
-      for (int j = 0; j < NT; ++j) bv[u][j] = *(const bf16x8*)(bptr[j] + k0 + 32 * u);
-      av[u] = arow_ok ? *(const bf16x8*)(aptr + k0 + 32 * u) : zero8;
+  for (int t = 0; t < S - 1; ++t)
+    if (t < nst) issue(t);
+  for (int t = 0; t < nst; ++t) {
+    // The refill of slot (t - 1) % S follows the reads of stage t - 1, which have completed: their
+    // values fed that stage's MFMAs.
+    if (t + S - 1 < nst) {
+      issue(t + S - 1);
+      wait_vmcnt<(S - 1) * T::NDMA>();
+    } else {
+      wait_vmcnt<0>();
     }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    const char* st = ring + (t % S) * T::STAGE_BYTES;
+    const int kmax = t == nst - 1 ? ktail : SK;
 #pragma unroll
-    for (int u = 0; u < DC_U; ++u)
+    for (int u = 0; u < U; ++u) {
+      if (32 * u >= kmax) break;
+      const int off = r16 * CPR * 16 + 16 * ((4 * u + kq) ^ T::sig(r16));
+      const bf16x8 av = *(const bf16x8*)(st + off);
 #pragma unroll
-      for (int j = 0; j < NT; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], bv[u][j], acc[j], 0, 0, 0);
-  }
-  for (; k0 < P.K; k0 += 32) {  // K is a multiple of 64: at most one short iteration
-    bf16x8 bv[NT];
-#pragma unroll
-    for (int j = 0; j < NT; ++j) bv[j] = *(const bf16x8*)(bptr[j] + k0);
-    const bf16x8 av = arow_ok ? *(const bf16x8*)(aptr + k0) : zero8;
-#pragma unroll
-    for (int j = 0; j < NT; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv[j], acc[j], 0, 0, 0);
+      for (int j = 0; j < NT; ++j) {
+        const bf16x8 bv = *(const bf16x8*)(st + (1 + j) * T::TILE_BYTES + off);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[j], 0, 0, 0);
+      }
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
   }
 
   // 16x16 C layout: lane holds column lane % 16, rows 4 (lane / 16) + i.
@@ -133,7 +183,7 @@ __global__ __launch_bounds__(256) void grouped_bf16_decode(GroupedArgs a, int nc
 
 template <bool GATE_UP>
 hipError_t launch(const GroupedArgs& a, int64_t max_tile_count, hipStream_t s) {
-  constexpr int BLOCK_COLS = 4 * (GATE_UP ? DC_NT / 2 * 16 : DC_NT * 16);
+  constexpr int BLOCK_COLS = DecodeTile<GATE_UP>::BLOCK_COLS;
   int nc = 0;
   for (int p = 0; p < 2; ++p)
     if (a.prob[p].out) nc = max(nc, (a.prob[p].ncols + BLOCK_COLS - 1) / BLOCK_COLS);

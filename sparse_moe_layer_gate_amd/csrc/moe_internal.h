@@ -30,6 +30,27 @@ struct Tile {
   int32_t rows;       // valid rows in this tile (1..BM)
 };
 
+// ---- device helpers shared by the kernels ----
+typedef __attribute__((address_space(3))) void lds_void;
+
+// float -> bfloat16 bits, round to nearest even (finite inputs).
+__device__ inline uint16_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ inline float bf16_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// SwiGLU of one intermediate column: silu(gate) * up.
+__device__ inline float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+// s_waitcnt with vmcnt = N and the other counters left at their maximum (gfx9 encoding).
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Profiling hooks (no-ops unless moe_profile_begin() was called).
 void prof_before(int stage, hipStream_t s);
 void prof_after(int stage, hipStream_t s);

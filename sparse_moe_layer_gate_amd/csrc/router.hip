@@ -21,24 +21,10 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ inline float load_as_f32(const float* p, int64_t i) { return p[i]; }
 __device__ inline float load_as_f32(const uint16_t* p, int64_t i) {
   return __uint_as_float((uint32_t)p[i] << 16);  // bf16 -> f32 is exact
-}
-
-__device__ inline uint16_t bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-__device__ inline float bf16_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
-
-template <int N>
-__device__ inline void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 // ---------------------------------------------------------------------------------------------
