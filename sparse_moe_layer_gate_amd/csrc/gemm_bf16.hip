@@ -22,9 +22,35 @@ namespace {
 #ifndef MOE_PF_GROUP_ROWS
 #define MOE_PF_GROUP_ROWS 4
 #endif
+// L2 line touches ahead of the ring (see PrefillTile::TOUCH): distance in K steps (0: off) for the
+// gate_up and down GEMMs, the smallest routed-expert row count that turns them on, and which operands
+// (bit 0: A, bit 1: B) are touched.
+#ifndef MOE_PF_TOUCH_GU
+#define MOE_PF_TOUCH_GU 0
+#endif
+#ifndef MOE_PF_TOUCH_DN
+#define MOE_PF_TOUCH_DN 2
+#endif
+#ifndef MOE_PF_TOUCH_MIN_ROWS
+#define MOE_PF_TOUCH_MIN_ROWS 1024
+#endif
+#ifndef MOE_PF_TOUCH_GU_OPS
+#define MOE_PF_TOUCH_GU_OPS 3
+#endif
+#ifndef MOE_PF_TOUCH_DN_OPS
+#define MOE_PF_TOUCH_DN_OPS 1
+#endif
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+template <bool V>
+struct BoolC {
+  static constexpr bool value = V;
+};
 
 template <int BM, int BK, int STAGES, bool GATE_UP>
 struct PrefillTile {
@@ -41,6 +67,14 @@ struct PrefillTile {
   static constexpr int COLS = GATE_UP ? BN / 2 : BN;  // output columns per block
   static_assert(TN % 2 == 0, "gate_up pairs gate and up column tiles inside a wave");
   static_assert(CPR == 8 || CPR == 4, "BK is 64 or 32");
+  // L2 warm-up: with a two-stage ring a step's operands have one step of compute to arrive, less
+  // than a miss to HBM takes. For tiles of large experts (whose B is shared by many row tiles and stays
+  // cached, so the A rows are what misses) each lane also touches one line of the selected operands
+  // TOUCH steps ahead (4-byte direct loads into a scratch word), so the later full loads hit L2.
+  // Measured: it pays for down on row-heavy experts; elsewhere the extra requests cost more.
+  static constexpr int TOUCH = STAGES == 2 ? (GATE_UP ? MOE_PF_TOUCH_GU : MOE_PF_TOUCH_DN) : 0;
+  static constexpr int TOUCH_OPS = GATE_UP ? MOE_PF_TOUCH_GU_OPS : MOE_PF_TOUCH_DN_OPS;  // bit 0: A, bit 1: B
+  static constexpr int NTOUCH = (TOUCH_OPS & 1) + ((TOUCH_OPS >> 1) & 1);
 
   // Chunk swizzle: the 16-byte chunk c of LDS row r is stored in slot c ^ swz(r). swz depends on
   // r mod 32 only, and any 8 (and any aligned 16) consecutive rows get distinct slots, so the MFMA
@@ -73,10 +107,16 @@ struct PrefillTile {
   }
 
   // The K loop for a wave whose first MI 32-row sub-tiles hold valid rows (MI = 0: loads only).
-  template <int MI>
+  template <int MI, bool TOUCHING>
   __device__ static __attribute__((always_inline)) void run(char* lds, const uint16_t* const (&srcA)[NA],
                                                             const uint16_t* const (&srcB)[NB], f32x16 (&acc)[TM][TN],
-                                                            int nk, int wave, int lane, int wm, int wn) {
+                                                            int nk, int wave, int lane, int wm, int wn,
+                                                            const uint16_t* touchA, const uint16_t* touchB,
+                                                            int* sink) {
+    auto touch = [&](int kstep) {
+      if (TOUCH_OPS & 1) __builtin_amdgcn_global_load_lds((const void*)(touchA + kstep * BK), (lds_void*)sink, 4, 0, 0);
+      if (TOUCH_OPS & 2) __builtin_amdgcn_global_load_lds((const void*)(touchB + kstep * BK), (lds_void*)sink, 4, 0, 0);
+    };
     const int sw = swz(lane & 31);
     const int a_off = (wm * WAVE_M + (lane & 31)) * ROWB;
     int b_off[TN];
@@ -85,19 +125,26 @@ struct PrefillTile {
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s)
       if (s < nk) issue(lds, srcA, srcB, s, wave);
+    if (TOUCHING && TOUCH < nk) touch(TOUCH);
     for (int kt = 0; kt < nk; ++kt) {
-      // Step kt's direct loads are this wave's oldest outstanding VMEM ops; once every wave has waited
-      // for its own and met at the barrier, step kt is in LDS. The barrier also ends every wave's reads
-      // of the stage that the next issue() refills (they fed MFMAs of step kt - 1). A plain s_barrier:
+      // Step kt's direct loads are this wave's oldest outstanding VMEM ops (only the two touches of
+      // step kt + TOUCH, issued right after them, may be newer); once every wave has waited for its
+      // own and met at the barrier, step kt is in LDS. The barrier also ends every wave's reads of the
+      // stage that the next issue() refills (they fed MFMAs of step kt - 1). A plain s_barrier:
       // __syncthreads() would add a vmcnt(0) wait and drain the prefetches of later steps.
-      if (kt + STAGES - 2 < nk)
+      if (TOUCHING && kt + TOUCH < nk)
+        wait_vmcnt<NTOUCH>();
+      else if (kt + STAGES - 2 < nk)
         wait_vmcnt<(STAGES - 2) * LPS>();
       else
         wait_vmcnt<0>();
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       __builtin_amdgcn_s_barrier();
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      if (kt + STAGES - 1 < nk) issue(lds, srcA, srcB, kt + STAGES - 1, wave);
+      if (kt + STAGES - 1 < nk) {
+        issue(lds, srcA, srcB, kt + STAGES - 1, wave);
+        if (TOUCHING && kt + 1 + TOUCH < nk) touch(kt + 1 + TOUCH);
+      }
       if (MI == 0) continue;
       const char* st = lds + (kt % STAGES) * STAGE_BYTES;
       bf16x8 af[2][MI > 0 ? MI : 1], bfr[2][TN];
@@ -155,6 +202,7 @@ __global__ __launch_bounds__(256, 1) void grouped_bf16_lds(GroupedArgs a, int nc
   constexpr int LDS_BYTES = STAGES * T::STAGE_BYTES > OUT_BYTES ? STAGES * T::STAGE_BYTES : OUT_BYTES;
   __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
   __shared__ float wrow[BM];
+  __shared__ int touch_sink[64];
 
   // Rasterization: logical ids walk GR row tiles down a column before moving right, so the blocks
   // one XCD runs together share GR-fold the B slices and (32 / GR)-fold the A slices.
@@ -205,6 +253,27 @@ __global__ __launch_bounds__(256, 1) void grouped_bf16_lds(GroupedArgs a, int nc
     }
     srcB[q] = base + (int64_t)tile.expert * P.b_stride + (int64_t)col * P.K + 8 * c;
   }
+  // The shared expert's down GEMM (every token) counts as large.
+  const bool touch_on = T::TOUCH > 0 && (tile.problem == 1 || !a.offsets ||
+                                         a.offsets[tile.expert + 1] - a.offsets[tile.expert] >= MOE_PF_TOUCH_MIN_ROWS);
+  // Line-touch sources: A row t (clamped to the tile) and B row t, at chunk 0.
+  const uint16_t* touchA;
+  const uint16_t* touchB;
+  {
+    int64_t g = (int64_t)tile.row_start + min(t, tile.rows - 1);
+    if (P.gather) g = a.sorted_pair[g] / a.k;
+    touchA = (const uint16_t*)P.A + g * P.lda;
+    const uint16_t* base;
+    int col;
+    if (GATE_UP) {
+      base = (const uint16_t*)(t % BN < BN / 2 ? P.B0 : P.B1);
+      col = min(col0 + t % (BN / 2), P.ncols - 1);
+    } else {
+      base = (const uint16_t*)P.B0;
+      col = min(col0 + t % BN, P.ncols - 1);
+    }
+    touchB = base + (int64_t)tile.expert * P.b_stride + (int64_t)col * P.K;
+  }
   if (!GATE_UP && t < BM) {
     const int r = min(t, tile.rows - 1);
     wrow[t] = P.scale_rows ? a.topk_w[a.sorted_pair[tile.row_start + r]] : 1.0f;
@@ -221,15 +290,23 @@ __global__ __launch_bounds__(256, 1) void grouped_bf16_lds(GroupedArgs a, int nc
   const int nk = P.K / BK;
   const int live_m = tile.rows - wm * WAVE_M;  // valid rows of this wave's slab
   const int mi = live_m <= 0 ? 0 : min(TM, (live_m + 31) / 32);
-#define MOE_PF_RUN run
-  switch (mi) {
-    case 0: T::template MOE_PF_RUN<0>(lds, srcA, srcB, acc, nk, wave, lane, wm, wn); break;
-    case 1: T::template MOE_PF_RUN<1>(lds, srcA, srcB, acc, nk, wave, lane, wm, wn); break;
-    case 2: T::template MOE_PF_RUN<(TM >= 2 ? 2 : 1)>(lds, srcA, srcB, acc, nk, wave, lane, wm, wn); break;
-    case 3: T::template MOE_PF_RUN<(TM >= 3 ? 3 : 1)>(lds, srcA, srcB, acc, nk, wave, lane, wm, wn); break;
-    default: T::template MOE_PF_RUN<TM>(lds, srcA, srcB, acc, nk, wave, lane, wm, wn); break;
-  }
-#undef MOE_PF_RUN
+  auto run = [&](auto mi_tag, auto touch_tag) {
+    T::template run<decltype(mi_tag)::value, decltype(touch_tag)::value>(lds, srcA, srcB, acc, nk, wave, lane, wm, wn,
+                                                                         touchA, touchB, touch_sink);
+  };
+  auto run_mi = [&](auto touch_tag) {
+    switch (mi) {
+      case 0: run(IntC<0>{}, touch_tag); break;
+      case 1: run(IntC<1>{}, touch_tag); break;
+      case 2: run(IntC<(TM >= 2 ? 2 : 1)>{}, touch_tag); break;
+      case 3: run(IntC<(TM >= 3 ? 3 : 1)>{}, touch_tag); break;
+      default: run(IntC<TM>{}, touch_tag); break;
+    }
+  };
+  if (T::TOUCH > 0 && touch_on)
+    run_mi(BoolC<true>{});
+  else
+    run_mi(BoolC<false>{});
 
   // Epilogue through LDS: each wave writes its bf16 results (SwiGLU / weight scale applied) into its
   // own padded region, then stores whole 16-byte row chunks, so a store instruction covers

@@ -271,6 +271,7 @@ moe_status moe_forward(const moe_config* cfg, int64_t N, const void* x, const mo
   g.sorted_pair = sorted_pair;
   g.topk_w = w;
   g.k = k;
+  g.offsets = at<int32_t>(ws, L.offsets);
   // gate_up + SwiGLU: routed rows gather x through sorted_pair; the shared expert reads x in order
   g.tiles = at<Tile>(ws, L.tiles0);
   g.n_tiles = at<int32_t>(ws, L.ntiles);

@@ -106,6 +106,7 @@ struct GroupedArgs {
   const int32_t* sorted_pair;
   const float* topk_w;
   int k;
+  const int32_t* offsets;  // routed experts' row offsets [E + 1] (or nullptr: every expert counts as large)
 };
 // Field-wise select keeps a problem descriptor in scalar registers (a dynamically indexed
 // kernel-argument array would be copied to scratch).
