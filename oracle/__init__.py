@@ -32,6 +32,8 @@ class OracleCfg(ctypes.Structure):
         ("alpha", ctypes.c_float),
         ("norm", ctypes.c_int32),
         ("eps", ctypes.c_float),
+        ("limit", ctypes.c_float),
+        ("alpha_on_output", ctypes.c_int32),
     ]
 
 
@@ -54,7 +56,7 @@ def lib():
         L.oracle_select.argtypes = [cp, i64, vp, vp, vp, vp, vp]
         L.oracle_select_margin.argtypes = [cp, i64, vp, vp, vp]
         L.oracle_dispatch.argtypes = [cp, i64, vp, vp, vp, vp, vp]
-        L.oracle_swiglu.argtypes = [ctypes.c_int32, ctypes.c_int32, vp, vp, vp, i32, vp, vp]
+        L.oracle_swiglu.argtypes = [ctypes.c_int32, ctypes.c_int32, vp, vp, vp, i32, ctypes.c_double, vp, vp]
         L.oracle_swiglu.restype = None
         L.oracle_forward_tokens.argtypes = [cp, i64, vp, vp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp]
         L.oracle_forward_expert_loop.argtypes = [cp, i64, vp, i32, vp, vp, vp, vp, vp, i32, vp, vp, vp]
@@ -67,8 +69,10 @@ def lib():
 
 
 def cfg_of(w) -> OracleCfg:
-    """Oracle config from any object with the fields D, E, G, TG, k, d, n_shared, alpha, norm, eps."""
-    return OracleCfg(w.D, w.E, w.G, w.TG, w.k, w.d, w.n_shared, float(w.alpha), int(bool(w.norm)), float(w.eps))
+    """Oracle config from any object with the fields D, E, G, TG, k, d, n_shared, alpha, norm, eps (and
+    optionally limit, alpha_on_output)."""
+    return OracleCfg(w.D, w.E, w.G, w.TG, w.k, w.d, w.n_shared, float(w.alpha), int(bool(w.norm)), float(w.eps),
+                     float(getattr(w, "limit", 0.0)), int(bool(getattr(w, "alpha_on_output", False))))
 
 
 def _dt(a: np.ndarray) -> int:
@@ -153,16 +157,17 @@ def dispatch(w, idx: np.ndarray):
     return counts, offsets, sorted_pair, inv_row
 
 
-def swiglu(gate, up, down, x) -> np.ndarray:
-    """One SwiGLU MLP on one token in double: down (SiLU(gate x) * up x)."""
+def swiglu(gate, up, down, x, limit: float = 0.0) -> np.ndarray:
+    """One SwiGLU MLP on one token in double: down (SiLU(a) * u), a = gate x, u = up x, clamped as
+    a = min(a, limit), u = clip(u, -limit, limit) when limit > 0."""
     gate, up, down = _c(gate), _c(up), _c(down)
     dt = _dt(gate)
     assert _dt(up) == dt and _dt(down) == dt
     dff, D = gate.shape
     xd = _c(x, np.float64)
     out = np.empty(D, np.float64)
-    lib().oracle_swiglu(D, dff, gate.ctypes.data, up.ctypes.data, down.ctypes.data, dt, xd.ctypes.data,
-                        out.ctypes.data)
+    lib().oracle_swiglu(D, dff, gate.ctypes.data, up.ctypes.data, down.ctypes.data, dt, float(limit),
+                        xd.ctypes.data, out.ctypes.data)
     return out
 
 

@@ -25,6 +25,8 @@ int oracle_check_cfg(const oracle_cfg* c) {
   if (c->TG < 1 || c->TG > c->G) return -1;
   if (c->G > 1 && c->E / c->G < 2) return -1; /* a group needs two members for its top-2 score */
   if (c->k > c->TG * (c->E / c->G)) return -1; /* kept groups must hold at least k experts */
+  if (!(c->limit >= 0.0f) || isinf(c->limit)) return -1;
+  if (c->alpha_on_output != 0 && c->alpha_on_output != 1) return -1;
   return 0;
 }
 
@@ -106,18 +108,20 @@ static void take_topk(const oracle_cfg* c, const token_work* tw, int32_t* idx) {
 
 /* "Group Router", eq. s-bar / w, and "MoE Forward", eq. w_{n,i}: the weights use the raw s of the
  * chosen experts (never s'), renormalised over the chosen set with eps in the denominator when
- * norm_topk_prob is set, then multiplied by alpha. */
+ * norm_topk_prob is set, then multiplied by alpha -- unless alpha goes on the routed output instead
+ * ("MoE Forward", Official code: one place or the other, never both). */
 static void weights(const oracle_cfg* c, const float* s_row, const int32_t* idx, float* w) {
+  const float a = c->alpha_on_output ? 1.0f : c->alpha;
   if (c->norm) {
     float sum = 0.0f;
     for (int slot = 0; slot < c->k; ++slot) sum = sum + s_row[idx[slot]];
     float den = sum + c->eps;
     for (int slot = 0; slot < c->k; ++slot) {
       float q = s_row[idx[slot]] / den;
-      w[slot] = c->alpha * q;
+      w[slot] = a * q;
     }
   } else {
-    for (int slot = 0; slot < c->k; ++slot) w[slot] = c->alpha * s_row[idx[slot]];
+    for (int slot = 0; slot < c->k; ++slot) w[slot] = a * s_row[idx[slot]];
   }
 }
 
@@ -188,8 +192,8 @@ int oracle_dispatch(const oracle_cfg* c, int64_t N, const int32_t* idx, int32_t*
   const int E = c->E, k = c->k;
   for (int e = 0; e < E; ++e) counts[e] = 0;
   for (int64_t i = 0; i < N * k; ++i) {
-    if (idx[i] < 0 || idx[i] >= E) return -1;
-    counts[idx[i]]++;
+    if (idx[i] < 0 || idx[i] > E) return -1;
+    if (idx[i] < E) counts[idx[i]]++;
   }
   offsets[0] = 0;
   for (int e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
@@ -198,6 +202,10 @@ int oracle_dispatch(const oracle_cfg* c, int64_t N, const int32_t* idx, int32_t*
   for (int64_t n = 0; n < N; ++n) {
     for (int slot = 0; slot < k; ++slot) {
       int64_t p = n * k + slot;
+      if (idx[p] == E) {  /* empty slot ("GLM-5 . Mixture of experts": id E is skipped) */
+        inv_row[p] = -1;
+        continue;
+      }
       int32_t pos = cursor[idx[p]]++;
       sorted_pair[pos] = (int32_t)p;
       inv_row[p] = pos;
@@ -207,10 +215,21 @@ int oracle_dispatch(const oracle_cfg* c, int64_t N, const int32_t* idx, int32_t*
   return 0;
 }
 
+/* SiLU(a) * u of one intermediate column; with limit > 0 the gate value is capped from above only and
+ * the up value clipped on both sides first ("Module 02 -- MoE: Capacity, Work, and Traffic", section 3). */
+static double swiglu_act(double g, double u, double limit) {
+  if (limit > 0.0) {
+    if (g > limit) g = limit;
+    if (u > limit) u = limit;
+    if (u < -limit) u = -limit;
+  }
+  return g / (1.0 + exp(-g)) * u;
+}
+
 /* "MoE Forward", eq. E_i: W_down (SiLU(W_gate x) (.) W_up x), bias-free; SiLU(z) = z / (1 + e^-z).
  * "Shared output": the shared expert is the same MLP with its own gate / up / down matrices. */
 void oracle_swiglu(int32_t D, int32_t dff, const void* gate, const void* up, const void* down, int wdt,
-                   const double* x, double* out) {
+                   double limit, const double* x, double* out) {
   double* h = (double*)malloc(sizeof(double) * (size_t)dff);
   for (int64_t j = 0; j < dff; ++j) {
     double g = 0.0, u = 0.0;
@@ -218,7 +237,7 @@ void oracle_swiglu(int32_t D, int32_t dff, const void* gate, const void* up, con
       g += widen(gate, wdt, j * D + t) * x[t];
       u += widen(up, wdt, j * D + t) * x[t];
     }
-    h[j] = g / (1.0 + exp(-g)) * u;
+    h[j] = swiglu_act(g, u, limit);
   }
   for (int64_t i = 0; i < D; ++i) {
     double o = 0.0;
@@ -236,11 +255,11 @@ static void routed_expert(const oracle_cfg* c, const void* gu, const void* dn, i
                           double* out) {
   const char* base = (const char*)gu;
   const void* up = base + (size_t)c->d * (size_t)c->D * elem_size(wdt);
-  oracle_swiglu(c->D, c->d, gu, up, dn, wdt, x, out);
+  oracle_swiglu(c->D, c->d, gu, up, dn, wdt, (double)c->limit, x, out);
 }
 
-/* "MoE Forward", eq. y_n: the alpha-scaled (inside w) routed sum over the chosen experts in slot order,
- * plus the shared expert at scale 1 on the same input. */
+/* "MoE Forward", eq. y_n: the alpha-scaled routed sum over the chosen experts in slot order, plus the
+ * shared expert at scale 1 on the same input. */
 int oracle_forward_tokens(const oracle_cfg* c, int64_t ntok, const int64_t* tokens, const void* x, int xdt,
                           const void* const* gate_up, const void* const* down, const void* sh_gate,
                           const void* sh_up, const void* sh_down, int wdt, const int32_t* idx, const float* w,
@@ -250,7 +269,7 @@ int oracle_forward_tokens(const oracle_cfg* c, int64_t ntok, const int64_t* toke
   for (int64_t i = 0; i < ntok; ++i)
     for (int64_t slot = 0; slot < k; ++slot) {
       int32_t e = idx[tokens[i] * k + slot];
-      if (e < 0 || e >= c->E || !gate_up[e] || !down[e]) return -1;
+      if (e < 0 || e > c->E || (e < c->E && (!gate_up[e] || !down[e]))) return -1;
     }
   if (c->n_shared > 0 && (!sh_gate || !sh_up || !sh_down)) return -1;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -262,12 +281,15 @@ int oracle_forward_tokens(const oracle_cfg* c, int64_t ntok, const int64_t* toke
     for (int64_t t = 0; t < D; ++t) xd[t] = widen(x, xdt, n * D + t);
     for (int64_t slot = 0; slot < k; ++slot) {
       int32_t e = idx[n * k + slot];
+      if (e == c->E) continue; /* empty slot */
       routed_expert(c, gate_up[e], down[e], wdt, xd, o);
       double ws = (double)w[n * k + slot];
       for (int64_t t = 0; t < D; ++t) acc[t] += ws * o[t];
     }
+    if (c->alpha_on_output)
+      for (int64_t t = 0; t < D; ++t) acc[t] *= (double)c->alpha;
     if (c->n_shared > 0) {
-      oracle_swiglu(c->D, c->d * c->n_shared, sh_gate, sh_up, sh_down, wdt, xd, o);
+      oracle_swiglu(c->D, c->d * c->n_shared, sh_gate, sh_up, sh_down, wdt, (double)c->limit, xd, o);
       for (int64_t t = 0; t < D; ++t) acc[t] += o[t];
     }
     for (int64_t t = 0; t < D; ++t) y[i * D + t] = (float)acc[t];
@@ -288,7 +310,7 @@ int oracle_forward_expert_loop(const oracle_cfg* c, int64_t N, const void* x, in
   if (oracle_check_cfg(c)) return -1;
   const int64_t D = c->D, k = c->k, E = c->E, d = c->d;
   for (int64_t p = 0; p < N * k; ++p)
-    if (idx[p] < 0 || idx[p] >= E || !gate_up[idx[p]] || !down[idx[p]]) return -1;
+    if (idx[p] < 0 || idx[p] > E || (idx[p] < E && (!gate_up[idx[p]] || !down[idx[p]]))) return -1;
   if (c->n_shared > 0 && (!sh_gate || !sh_up || !sh_down)) return -1;
   double* acc = (double*)calloc((size_t)(N * D), sizeof(double));
   double* xd = (double*)malloc(sizeof(double) * (size_t)(N * D));
@@ -314,6 +336,8 @@ int oracle_forward_expert_loop(const oracle_cfg* c, int64_t N, const void* x, in
       u_ptr = (const char*)gate_up[e] + (size_t)d * (size_t)D * elem_size(wdt);
       dn_ptr = down[e];
     } else {
+      if (c->alpha_on_output)
+        for (int64_t i = 0; i < N * D; ++i) acc[i] *= (double)c->alpha;
       if (c->n_shared == 0) break;
       for (int64_t n = 0; n < N; ++n) {
         tok[m] = n;
@@ -335,7 +359,7 @@ int oracle_forward_expert_loop(const oracle_cfg* c, int64_t N, const void* x, in
           g += widen(g_ptr, wdt, j * D + t) * xr[t];
           u += widen(u_ptr, wdt, j * D + t) * xr[t];
         }
-        h[i * dff + j] = g / (1.0 + exp(-g)) * u;
+        h[i * dff + j] = swiglu_act(g, u, (double)c->limit);
       }
     }
 #pragma omp parallel for schedule(static)

@@ -32,8 +32,21 @@
  * notes): discarded groups are excluded (the "-inf" reading of the group
  * mask); ties go to the lower expert / group index; the k output slots are in
  * (s' descending, index ascending) order and that order fixes the sum in the
- * weight denominator; alpha is applied inside the weights, once; eps is the
- * float32 nearest 1e-20; the SwiGLU is unclamped.
+ * weight denominator; alpha is applied once, inside the weights unless
+ * alpha_on_output asks for it on the routed sum; eps is the float32 nearest
+ * 1e-20; the SwiGLU is plain unless limit > 0.
+ *
+ * Variants ("MoE Forward", Official code: the router and the routed output as
+ * separate places alpha may sit; "GLM-5 . Mixture of experts": the loop form
+ * that skips the expert id E; "Module 02 -- MoE: Capacity, Work, and Traffic",
+ * section 3: the clamped SwiGLU of that checkpoint):
+ *  - alpha_on_output = 1: the weights are s / (sum s + eps) and the routed sum
+ *    is multiplied by alpha (the shared expert still enters at scale 1);
+ *  - limit > 0: every expert, routed or shared, clamps its gate projection
+ *    from above at limit (no lower bound) and its up projection to
+ *    [-limit, limit] before SiLU(gate) * up;
+ *  - routing given by the caller may hold the id E in a slot: that slot adds
+ *    nothing (an empty slot).
  */
 #ifndef MOE_ORACLE_H
 #define MOE_ORACLE_H
@@ -58,6 +71,8 @@ typedef struct {
   float alpha;      /* routed_scaling_factor */
   int32_t norm;     /* norm_topk_prob */
   float eps;        /* added to the weight denominator */
+  float limit;      /* SwiGLU clamp bound; 0 = plain SwiGLU */
+  int32_t alpha_on_output; /* 1: alpha scales the routed sum instead of the weights */
 } oracle_cfg;
 
 /* 0 if the configuration is one the oracle can evaluate, else -1. */
@@ -79,18 +94,20 @@ int oracle_select(const oracle_cfg* c, int64_t N, const float* s, const float* b
  * next group score. A token whose gap exceeds the score error cannot change its routing. */
 int oracle_select_margin(const oracle_cfg* c, int64_t N, const float* s, const float* b, double* margin);
 
-/* counts[E], offsets[E+1] (exclusive scan), sorted_pair[N*k] (flat n*k+slot, tokens ascending inside each
- * expert), inv_row[N*k] (position of each (n, slot) in that order). */
+/* counts[E], offsets[E+1] (exclusive scan), sorted_pair[offsets[E]] (flat n*k+slot, tokens ascending inside
+ * each expert), inv_row[N*k] (position of each (n, slot) in that order; -1 for an empty slot, id E). */
 int oracle_dispatch(const oracle_cfg* c, int64_t N, const int32_t* idx, int32_t* counts, int32_t* offsets,
                     int32_t* sorted_pair, int32_t* inv_row);
 
-/* One SwiGLU MLP on one token, in double: out[D] = down (SiLU(gate x) * (up x)).
+/* One SwiGLU MLP on one token, in double: out[D] = down (SiLU(a) * u) with a = gate x, u = up x, clamped
+ * as a = min(a, limit), u = min(max(u, -limit), limit) when limit > 0.
  * gate, up: [dff, D]; down: [D, dff]; element type wdt. */
 void oracle_swiglu(int32_t D, int32_t dff, const void* gate, const void* up, const void* down, int wdt,
-                   const double* x, double* out);
+                   double limit, const double* x, double* out);
 
 /* Per-token form of the layer output for the listed tokens, given routing (idx, w for all N tokens):
- * y[i] = float( sum_slot w * E_idx(x_n) + E_sh(x_n) ), n = tokens[i].
+ * y[i] = float( A * sum_slot w * E_idx(x_n) + E_sh(x_n) ), n = tokens[i], A = alpha if alpha_on_output
+ * else 1; slots holding id E are empty.
  * gate_up[e] -> [2d, D], down[e] -> [D, d] (entries may be NULL for experts no listed token uses). */
 int oracle_forward_tokens(const oracle_cfg* c, int64_t ntok, const int64_t* tokens, const void* x, int xdt,
                           const void* const* gate_up, const void* const* down, const void* sh_gate,
@@ -98,7 +115,8 @@ int oracle_forward_tokens(const oracle_cfg* c, int64_t ntok, const int64_t* toke
                           float* y);
 
 /* Per-expert loop form over all N tokens: for each expert with at least one token, add w * E_e(x_n)
- * into a double accumulator, expert by expert; then add the shared expert; round once. */
+ * into a double accumulator, expert by expert; scale it by A (as above), add the shared expert; round
+ * once. Slots holding id E are skipped. */
 int oracle_forward_expert_loop(const oracle_cfg* c, int64_t N, const void* x, int xdt,
                                const void* const* gate_up, const void* const* down, const void* sh_gate,
                                const void* sh_up, const void* sh_down, int wdt, const int32_t* idx,

@@ -44,6 +44,10 @@ class Workload:
     seed: int = 0
     skew: float = 0.0  # std of the per-expert offset added to every element of a router row
     x_id: int = ID_X
+    limit: float = 0.0  # SwiGLU clamp bound (0: plain SwiGLU)
+    alpha_on_output: bool = False  # alpha scales the routed sum instead of the weights
+    outlier_every: int = 0  # every outlier_every-th token (0: none) is scaled by outlier_scale
+    outlier_scale: float = 32.0  # a power of two, so the scaled bf16 values stay exact
 
     @property
     def d_sh(self) -> int:
@@ -66,8 +70,14 @@ WORKLOADS = {
     # GLM-5-shaped decode step: the prefill weights, 32 fresh tokens.
     "glm5_decode": Workload("glm5_decode", N=32, D=6144, E=256, G=8, TG=4, k=8, d=2048, alpha=2.5,
                             x_id=ID_X_DECODE),
+    # The 288-expert shape with the clamped SwiGLU (bound 10): a batch of 32 decode requests, and a prefill.
+    "glm53_flash_decode": Workload("glm53_flash_decode", N=32, D=4096, E=288, G=1, TG=1, k=8, d=2048, alpha=2.5,
+                                   limit=10.0, x_id=ID_X_DECODE),
+    "glm53_flash_prefill": Workload("glm53_flash_prefill", N=8192, D=4096, E=288, G=1, TG=1, k=8, d=2048,
+                                    alpha=2.5, limit=10.0),
 }
-WORKLOAD_ORDER = ["tiny_fp32", "air_prefill", "glm45_prefill_skewed", "glm5_prefill", "glm5_decode"]
+WORKLOAD_ORDER = ["tiny_fp32", "air_prefill", "glm45_prefill_skewed", "glm5_prefill", "glm5_decode",
+                  "glm53_flash_decode", "glm53_flash_prefill"]
 
 # ---------------------------------------------------------------------------------------------
 _host = None
@@ -160,9 +170,18 @@ def bf16_to_f32(a: np.ndarray) -> np.ndarray:
 
 
 def x_host(w: Workload, first: int = 0, count: int | None = None) -> np.ndarray:
-    """Tokens first..first+count of x, shape [count, D] (float32, or bf16 bits)."""
+    """Tokens first..first+count of x, shape [count, D] (float32, or bf16 bits). Outlier tokens (every
+    outlier_every-th, counting from token 0) are multiplied by outlier_scale, a power of two."""
     count = w.N - first if count is None else count
-    return normal(w.seed, w.x_id, first * w.D, count * w.D, 1.0, w.dtype).reshape(count, w.D)
+    x = normal(w.seed, w.x_id, first * w.D, count * w.D, 1.0, w.dtype).reshape(count, w.D)
+    if w.outlier_every > 0:
+        rows = [i for i in range(count) if (first + i) % w.outlier_every == 0]
+        if rows:
+            if w.dtype == "bf16":
+                x[rows] = f32_to_bf16(bf16_to_f32(x[rows]) * np.float32(w.outlier_scale))
+            else:
+                x[rows] = x[rows] * np.float32(w.outlier_scale)
+    return x
 
 
 def router_host(w: Workload) -> tuple[np.ndarray, np.ndarray]:

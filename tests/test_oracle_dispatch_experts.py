@@ -48,9 +48,11 @@ def test_dispatch_invariants():
 
 
 def test_dispatch_rejects_out_of_range():
+    """Ids outside [0, E] are invalid (E itself is the empty slot, covered in test_oracle_variants)."""
     c = cfg(E=4, k=2)
-    with pytest.raises(ValueError):
-        oracle.dispatch(c, np.array([[0, 4]], np.int32))
+    for bad in (5, -1):
+        with pytest.raises(ValueError):
+            oracle.dispatch(c, np.array([[0, bad]], np.int32))
 
 
 def test_swiglu_identity_closed_form():
