@@ -15,7 +15,10 @@
  *    experts plus the shared one.
  *  - "GLM-5 . Mixture of experts" and "Shared output": the module layout (router,
  *    routed experts, one shared MLP of width n_shared * d) and the per-expert
- *    token lists that dispatch builds.
+ *    token lists that dispatch builds; the expert loop skips the id E, which
+ *    marks an empty slot in routing given by the caller.
+ *  - "Module 02 -- MoE: Capacity, Work, and Traffic", section 3: the clamped
+ *    SwiGLU of that checkpoint (swiglu_limit below).
  *
  * Conventions for every call:
  *  - Buffers: all tensor pointers are device pointers (HBM), row-major and
@@ -34,8 +37,9 @@
  *    top-k; ties go to the lower expert / group index (IEEE comparison, so +0
  *    equals -0); the k slots are in (s' descending, index ascending) order, and
  *    that order fixes the summation order of the weight denominator; alpha is
- *    applied inside the weights, once; eps is added to the denominator as a
- *    float32 (1e-20 rounds to 9.99999968e-21).
+ *    applied once, inside the weights unless alpha_on_output moves it to the
+ *    routed sum; eps is added to the denominator as a float32 (1e-20 rounds to
+ *    9.99999968e-21).
  */
 #ifndef SPARSE_MOE_LAYER_GATE_AMD_MOE_H
 #define SPARSE_MOE_LAYER_GATE_AMD_MOE_H
@@ -72,6 +76,14 @@ typedef struct {
   int32_t norm_topk_prob;        /* 0 or 1 */
   float eps;                     /* added to the weight denominator (1e-20 on the pages) */
   int32_t dtype;                 /* moe_dtype of x, the expert weights and y */
+  /* Where alpha goes ("MoE Forward", Official code: inside the router or on the routed output, never
+   * both). 0: w = alpha * s / (sum s + eps). 1: w = s / (sum s + eps), and the combine multiplies the
+   * routed sum by alpha before adding the shared expert. */
+  int32_t alpha_on_output;
+  /* Clamped SwiGLU ("Module 02 -- MoE: Capacity, Work, and Traffic", section 3), in every expert, routed
+   * and shared: with L = swiglu_limit > 0, gate = min(gate, L) (no lower bound) and
+   * up = min(max(up, -L), L) before SiLU(gate) * up. 0: plain SwiGLU. Finite and >= 0. */
+  float swiglu_limit;
 } moe_config;
 
 /* Device pointers to the layer's weights, in the pages' canonical layouts. */
@@ -102,7 +114,7 @@ size_t moe_workspace_size(const moe_config* cfg, int64_t N);
  *   e_bias   [E] float32
  *   scores   [N, E] float32: written with s (default) or read (MOE_ROUTE_SCORES_IN)
  *   topk_idx [N, k] int32 out: the chosen experts in slot order
- *   topk_w   [N, k] float32 out: their weights, alpha included
+ *   topk_w   [N, k] float32 out: their weights, alpha included (unless alpha_on_output)
  *   workspace, ws_bytes: scratch of at least moe_workspace_size(cfg, N) bytes (unused, may be NULL,
  *            with MOE_ROUTE_SCORES_IN)
  * The logits are float32 dot products (bf16 activations: exact products of x with an exact three-piece
@@ -115,9 +127,9 @@ moe_status moe_route(const moe_config* cfg, int64_t N, const void* x, const floa
 
 /* Token-choice dispatch: per-expert token lists in the per-expert loop form of "GLM-5 . Mixture of
  * experts", as counts, an exclusive scan and a stable placement (tokens ascending inside each expert).
- *   topk_idx    [N, k] int32 in: expert ids in [0, E)
+ *   topk_idx    [N, k] int32 in: expert ids in [0, E); E marks an empty slot
  *   counts      [E] int32 out: (token, slot) pairs per expert
- *   offsets     [E + 1] int32 out: exclusive scan of counts; offsets[E] = N * k
+ *   offsets     [E + 1] int32 out: exclusive scan of counts; offsets[E] = N * k less the empty slots
  *   sorted_pair [N * k] int32 out: the flat pair index n * k + slot at each expert-sorted position
  *   inv_row     [N * k] int32 out: the position of each pair (inverse of sorted_pair)
  * Pairs whose id is outside [0, E) are left out of the lists (inv_row = -1); the lists are then
@@ -135,6 +147,19 @@ moe_status moe_dispatch(const moe_config* cfg, int64_t N, const int32_t* topk_id
 moe_status moe_forward(const moe_config* cfg, int64_t N, const void* x, const moe_weights* w, void* y,
                        int32_t* topk_idx_out, float* topk_w_out, int32_t* counts_out, void* workspace,
                        size_t ws_bytes, void* stream);
+
+/* The layer with routing given by the caller ("MoE Forward", Official code: the experts take x, the
+ * top-k indices and the top-k weights; "GLM-5 . Mixture of experts": the expert loop skips id E):
+ * dispatch, routed experts, combine and shared expert as in moe_forward, without the router.
+ *   topk_idx [N, k] int32 in: expert ids; E (or any id outside [0, E)) marks an empty slot, which
+ *            adds nothing
+ *   topk_w   [N, k] float32 in: the weights, used as given (alpha is applied on the routed sum only
+ *            when cfg->alpha_on_output is 1)
+ *   x, y, counts_out, workspace, ws_bytes, stream: as for moe_forward.
+ * Deterministic: the same inputs give bit-identical outputs. */
+moe_status moe_forward_routed(const moe_config* cfg, int64_t N, const void* x, const moe_weights* w,
+                              const int32_t* topk_idx, const float* topk_w, void* y, int32_t* counts_out,
+                              void* workspace, size_t ws_bytes, void* stream);
 
 /* Static string naming a status. */
 const char* moe_status_str(moe_status status);

@@ -18,8 +18,9 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_F32, MOE_BF16 = 0, 1
 MOE_ROUTE_SCORES_IN = 1
 
-EXPORTED = ["moe_check_config", "moe_workspace_size", "moe_route", "moe_dispatch", "moe_forward", "moe_status_str",
-            "moe_profile_begin", "moe_profile_end", "moe_stage_name", "moe_stage_count"]
+EXPORTED = ["moe_check_config", "moe_workspace_size", "moe_route", "moe_dispatch", "moe_forward",
+            "moe_forward_routed", "moe_status_str", "moe_profile_begin", "moe_profile_end", "moe_stage_name",
+            "moe_stage_count"]
 
 
 class MoeError(RuntimeError):
@@ -41,6 +42,8 @@ class MoeConfig(ctypes.Structure):
         ("norm_topk_prob", ctypes.c_int32),
         ("eps", ctypes.c_float),
         ("dtype", ctypes.c_int32),
+        ("alpha_on_output", ctypes.c_int32),
+        ("swiglu_limit", ctypes.c_float),
     ]
 
 
@@ -69,6 +72,8 @@ def lib():
         L.moe_dispatch.argtypes = [cp, i64, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.moe_dispatch.restype = ctypes.c_int
         L.moe_forward.argtypes = [cp, i64, vp, ctypes.POINTER(MoeWeights), vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.moe_forward_routed.argtypes = [cp, i64, vp, ctypes.POINTER(MoeWeights), vp, vp, vp, vp, vp,
+                                         ctypes.c_size_t, vp]
         L.moe_forward.restype = ctypes.c_int
         L.moe_status_str.argtypes = [ctypes.c_int]
         L.moe_status_str.restype = ctypes.c_char_p
@@ -84,16 +89,21 @@ def lib():
     return _lib
 
 
-def make_config(D, E, G, TG, k, d, n_shared=1, alpha=1.0, norm=True, eps=1e-20, dtype="bf16") -> MoeConfig:
+def make_config(D, E, G, TG, k, d, n_shared=1, alpha=1.0, norm=True, eps=1e-20, dtype="bf16",
+                alpha_on_output=False, limit=0.0) -> MoeConfig:
     """moe_config from the pages' config fields (hidden_size, n_routed_experts, n_group, topk_group,
-    num_experts_per_tok, moe_intermediate_size, n_shared_experts, routed_scaling_factor, norm_topk_prob)."""
+    num_experts_per_tok, moe_intermediate_size, n_shared_experts, routed_scaling_factor, norm_topk_prob),
+    where alpha goes, and the SwiGLU clamp bound (0: none)."""
     dt = {"bf16": MOE_BF16, "f32": MOE_F32}[dtype] if isinstance(dtype, str) else int(dtype)
-    return MoeConfig(D, E, G, TG, k, d, n_shared, float(alpha), int(bool(norm)), float(eps), dt)
+    return MoeConfig(D, E, G, TG, k, d, n_shared, float(alpha), int(bool(norm)), float(eps), dt,
+                     int(bool(alpha_on_output)), float(limit))
 
 
 def config_of(w) -> MoeConfig:
-    """moe_config from an object with fields D, E, G, TG, k, d, n_shared, alpha, norm, eps, dtype."""
-    return make_config(w.D, w.E, w.G, w.TG, w.k, w.d, w.n_shared, w.alpha, w.norm, w.eps, w.dtype)
+    """moe_config from an object with fields D, E, G, TG, k, d, n_shared, alpha, norm, eps, dtype (and
+    optionally alpha_on_output, limit)."""
+    return make_config(w.D, w.E, w.G, w.TG, w.k, w.d, w.n_shared, w.alpha, w.norm, w.eps, w.dtype,
+                       getattr(w, "alpha_on_output", False), getattr(w, "limit", 0.0))
 
 
 def moe_status_str(status: int) -> str:
@@ -195,7 +205,8 @@ def moe_dispatch(cfg: MoeConfig, N: int, topk_idx, counts, offsets, sorted_pair,
 
 
 def weights_struct(cfg: MoeConfig, w: dict) -> MoeWeights:
-    """MoeWeights from a dict of device tensors: w_router, e_bias, gate_up, down, sh_gate, sh_up, sh_down."""
+    """MoeWeights from a dict of device tensors: w_router, e_bias, gate_up, down, sh_gate, sh_up, sh_down
+    (the router pair may be absent for moe_forward_routed)."""
     import torch
 
     E, D, d = cfg.n_routed_experts, cfg.hidden_size, cfg.moe_intermediate_size
@@ -203,8 +214,8 @@ def weights_struct(cfg: MoeConfig, w: dict) -> MoeWeights:
     adt = _act_dtype(cfg)
     sh = cfg.n_shared_experts > 0
     return MoeWeights(
-        _ptr(w["w_router"], "w_router", torch.float32, (E, D)),
-        _ptr(w["e_bias"], "e_bias", torch.float32, (E,)),
+        _ptr(w.get("w_router"), "w_router", torch.float32, (E, D), required=False),
+        _ptr(w.get("e_bias"), "e_bias", torch.float32, (E,), required=False),
         _ptr(w["gate_up"], "gate_up", adt, (E, 2 * d, D)),
         _ptr(w["down"], "down", adt, (E, D, d)),
         _ptr(w.get("sh_gate"), "sh_gate", adt, (dsh, D), required=sh) if sh else None,
@@ -233,6 +244,29 @@ def moe_forward(cfg: MoeConfig, N: int, x, weights, y, workspace, topk_idx_out=N
         workspace.numel(),
         _stream(stream))
     _check(st, "moe_forward")
+
+
+def moe_forward_routed(cfg: MoeConfig, N: int, x, weights, topk_idx, topk_w, y, workspace, counts_out=None,
+                       stream=None):
+    """The layer with routing given by the caller: topk_idx [N, k] int32 (id E = empty slot), topk_w [N, k]
+    float32 used as given."""
+    import torch
+
+    E, D, k = cfg.n_routed_experts, cfg.hidden_size, cfg.num_experts_per_tok
+    ws = weights if isinstance(weights, MoeWeights) else weights_struct(cfg, weights)
+    adt = _act_dtype(cfg)
+    st = lib().moe_forward_routed(
+        ctypes.byref(cfg), int(N),
+        _ptr(x, "x", adt, (N, D)),
+        ctypes.byref(ws),
+        _ptr(topk_idx, "topk_idx", torch.int32, (N, k)),
+        _ptr(topk_w, "topk_w", torch.float32, (N, k)),
+        _ptr(y, "y", adt, (N, D)),
+        _ptr(counts_out, "counts_out", torch.int32, (E,), required=False),
+        _ptr(workspace, "workspace", torch.uint8),
+        workspace.numel(),
+        _stream(stream))
+    _check(st, "moe_forward_routed")
 
 
 def stage_names() -> list:

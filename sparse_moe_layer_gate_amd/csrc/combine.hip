@@ -1,7 +1,8 @@
 // Combine ("MoE Forward", eq. y_n): y_n = sum over the k slots of the weighted expert rows (already
 // scaled by w in the down GEMM) + the shared expert's row, accumulated in float32 in slot order and
-// then the shared term, rounded once to the output type. No atomics: the same inputs always give the
-// same bits.
+// then the shared term, rounded once to the output type. When alpha sits on the routed output
+// ("MoE Forward", Official code) the slot sum is multiplied by it before the shared term is added.
+// Empty slots (inv_row < 0) add nothing. No atomics: the same inputs always give the same bits.
 #include <hip/hip_runtime.h>
 
 #include "moe_internal.h"
@@ -42,7 +43,7 @@ __device__ inline void store8(float* p, const float* acc) {
 template <typename T>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ Y, const T* __restrict__ Ysh,
                                                       const int32_t* __restrict__ inv_row, int k, int D,
-                                                      T* __restrict__ y) {
+                                                      float alpha_out, T* __restrict__ y) {
   __shared__ int rows[MAX_K];
   const int64_t n = blockIdx.x;
   if (threadIdx.x < k) rows[threadIdx.x] = inv_row[n * k + threadIdx.x];
@@ -53,6 +54,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ Y, c
       const int r = rows[slot];
       if (r >= 0) add8(acc, Y + (int64_t)r * D + c);
     }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = __fmul_rn(acc[i], alpha_out);  // exact when alpha_out == 1
     if (Ysh) add8(acc, Ysh + n * D + c);
     store8(y + n * D + c, acc);
   }
@@ -61,13 +64,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ Y, c
 }  // namespace
 
 hipError_t launch_combine(int dtype, const void* Y, const void* Ysh, const int32_t* inv_row, int64_t N, int k, int D,
-                          void* y, hipStream_t s) {
+                          float alpha_out, void* y, hipStream_t s) {
   if (dtype == MOE_F32)
     hipLaunchKernelGGL(combine_kernel<float>, dim3((unsigned)N), dim3(256), 0, s, (const float*)Y, (const float*)Ysh,
-                       inv_row, k, D, (float*)y);
+                       inv_row, k, D, alpha_out, (float*)y);
   else
     hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3((unsigned)N), dim3(256), 0, s, (const uint16_t*)Y,
-                       (const uint16_t*)Ysh, inv_row, k, D, (uint16_t*)y);
+                       (const uint16_t*)Ysh, inv_row, k, D, alpha_out, (uint16_t*)y);
   return hipGetLastError();
 }
 

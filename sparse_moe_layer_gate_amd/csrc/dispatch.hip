@@ -161,7 +161,18 @@ __global__ __launch_bounds__(256) void place_kernel(const int32_t* __restrict__ 
   }
 }
 
+__global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* __restrict__ p, int64_t n, int32_t v) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = v;
+}
+
 }  // namespace
+
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = min((n + 255) / 256, (int64_t)1024);
+  hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
 
 hipError_t launch_count(const int32_t* idx, int64_t N, int k, int E, int32_t* chunk_counts, hipStream_t s) {
   const int nchunks = (int)((N + CH - 1) / CH);

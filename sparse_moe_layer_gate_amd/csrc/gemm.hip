@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256) void grouped_f32(GroupedArgs a, int ncol_max) 
       const int64_t orow = (int64_t)tile.row_start + row;
       if (GATE_UP) {
         const int col = col0 + wn * 16 + (lane & 15);
-        if (col < P.ncols) out[orow * P.ldo + col] = silu_mul(acc[i][0][q], acc[i][1][q]);
+        if (col < P.ncols) out[orow * P.ldo + col] = swiglu(acc[i][0][q], acc[i][1][q], a.swiglu_limit);
       } else {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {

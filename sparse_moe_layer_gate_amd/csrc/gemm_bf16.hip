@@ -326,7 +326,7 @@ __global__ __launch_bounds__(256, 1) void grouped_bf16_lds(GroupedArgs a, int nc
       if (GATE_UP) {
 #pragma unroll
         for (int j = 0; j < TN / 2; ++j)
-          stage_out[row * OPITCH + j * 32 + (lane & 31)] = bf16_rne(silu_mul(acc[i][j][r], acc[i][j + TN / 2][r]));
+          stage_out[row * OPITCH + j * 32 + (lane & 31)] = bf16_rne(swiglu(acc[i][j][r], acc[i][j + TN / 2][r], a.swiglu_limit));
       } else {
         const float sc = wrow[min(wm * WAVE_M + row, BM - 1)];
 #pragma unroll

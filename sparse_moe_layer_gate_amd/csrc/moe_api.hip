@@ -24,6 +24,8 @@ moe_status check_cfg(const moe_config* c) {
   if (c->norm_topk_prob != 0 && c->norm_topk_prob != 1) return MOE_ERR_INVALID_ARG;
   if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (!std::isfinite(c->routed_scaling_factor) || !std::isfinite(c->eps) || c->eps < 0.f) return MOE_ERR_INVALID_ARG;
+  if (c->alpha_on_output != 0 && c->alpha_on_output != 1) return MOE_ERR_INVALID_ARG;
+  if (!std::isfinite(c->swiglu_limit) || c->swiglu_limit < 0.f) return MOE_ERR_INVALID_ARG;
   if (E > kMaxE || G > kMaxG || k > kMaxK) return MOE_ERR_UNSUPPORTED;
   if (D % 64 != 0 || d % 64 != 0) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)d * c->n_shared_experts > (1 << 24)) return MOE_ERR_UNSUPPORTED;
@@ -143,9 +145,10 @@ moe_status route_impl(const moe_config* c, int64_t N, const void* x, const float
     if (L.rp.split) MOE_TRY(ST_ROUTER_SPLIT, launch_router_split(wg, E, D, w3, s));
     MOE_TRY(ST_LOGITS, launch_logits(c->dtype, L.rp, x, wg, w3, N, D, E, part, s));
   }
+  // alpha on the routed output instead: the weights carry a factor 1, which the product leaves exact
+  const float alpha_w = c->alpha_on_output ? 1.0f : c->routed_scaling_factor;
   MOE_TRY(ST_SELECT, launch_select(scores, part, L.rp.ks, bias, N, E, c->n_group, c->topk_group,
-                                   c->num_experts_per_tok, c->routed_scaling_factor, c->norm_topk_prob, c->eps, idx, w,
-                                   s));
+                                   c->num_experts_per_tok, alpha_w, c->norm_topk_prob, c->eps, idx, w, s));
   return MOE_OK;
 }
 
@@ -160,6 +163,54 @@ moe_status dispatch_impl(const moe_config* c, int64_t N, const int32_t* idx, int
   MOE_TRY(ST_SCAN, launch_scan(at<int32_t>(ws, L.chunk_counts), nchunks, N, k, E, c->n_shared_experts > 0, counts,
                                offsets, at<int32_t>(ws, L.chunk_base), t0, t1, s));
   MOE_TRY(ST_PLACE, launch_place(idx, N, k, E, at<int32_t>(ws, L.chunk_base), sorted_pair, inv_row, s));
+  return MOE_OK;
+}
+
+// Routed experts, shared expert and combine for routing (idx, w) already dispatched into the workspace.
+moe_status experts_impl(const moe_config* cfg, int64_t N, const void* x, const moe_weights* wt, const float* w,
+                        void* y, void* ws, const Workspace& L, hipStream_t s) {
+  const int k = cfg->num_experts_per_tok, D = cfg->hidden_size;
+  const int d = cfg->moe_intermediate_size, dsh = d * cfg->n_shared_experts;
+  const int64_t es = cfg->dtype == MOE_F32 ? 4 : 2;
+  const bool shared = cfg->n_shared_experts > 0;
+  GroupedArgs g{};
+  g.sorted_pair = at<int32_t>(ws, L.sorted_pair);
+  g.topk_w = w;
+  g.k = k;
+  g.offsets = at<int32_t>(ws, L.offsets);
+  g.swiglu_limit = cfg->swiglu_limit;
+  // gate_up + SwiGLU: routed rows gather x through sorted_pair; the shared expert reads x in order
+  g.tiles = at<Tile>(ws, L.tiles0);
+  g.n_tiles = at<int32_t>(ws, L.ntiles);
+  g.bm = L.bm0;
+  g.prob[0] = ExpertProblem{x, D, 1, wt->gate_up, (const char*)wt->gate_up + es * (int64_t)d * D, 2LL * d * D, D, d,
+                            at<void>(ws, L.H), d, 0};
+  if (shared)
+    g.prob[1] = ExpertProblem{x, D, 0, wt->sh_gate, wt->sh_up, 0, D, dsh, at<void>(ws, L.Hsh), dsh, 0};
+  MOE_TRY(ST_GATE_UP, launch_gate_up(cfg->dtype, g, L.max_tiles0, s));
+  // down + mixture weight (routed) / weight 1 (shared)
+  g.tiles = at<Tile>(ws, L.tiles1);
+  g.n_tiles = at<int32_t>(ws, L.ntiles) + 1;
+  g.bm = L.bm1;
+  g.prob[0] = ExpertProblem{at<void>(ws, L.H), d, 0, wt->down, nullptr, (int64_t)D * d, d, D, at<void>(ws, L.Y), D, 1};
+  if (shared)
+    g.prob[1] = ExpertProblem{at<void>(ws, L.Hsh), dsh, 0, wt->sh_down, nullptr, 0, dsh, D, at<void>(ws, L.Ysh), D, 0};
+  MOE_TRY(ST_DOWN, launch_down(cfg->dtype, g, L.max_tiles1, s));
+  const float alpha_out = cfg->alpha_on_output ? cfg->routed_scaling_factor : 1.0f;
+  MOE_TRY(ST_COMBINE, launch_combine(cfg->dtype, at<void>(ws, L.Y), shared ? at<void>(ws, L.Ysh) : nullptr,
+                                     at<int32_t>(ws, L.inv_row), N, k, D, alpha_out, y, s));
+  return MOE_OK;
+}
+
+// Host checks shared by the forward entry points: x, y and the expert weights.
+moe_status check_expert_args(const moe_config* cfg, const void* x, const moe_weights* wt, const void* y) {
+  const bool shared = cfg->n_shared_experts > 0;
+  if (!x || !y || !wt->gate_up || !wt->down) return MOE_ERR_INVALID_ARG;
+  if (shared && (!wt->sh_gate || !wt->sh_up || !wt->sh_down)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(wt->gate_up) || !aligned16(wt->down)) return MOE_ERR_INVALID_ARG;
+  if (shared && (!aligned16(wt->sh_gate) || !aligned16(wt->sh_up) || !aligned16(wt->sh_down)))
+    return MOE_ERR_INVALID_ARG;
+  if (x == y) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
 }
 
@@ -223,9 +274,8 @@ moe_status moe_dispatch(const moe_config* cfg, int64_t N, const int32_t* topk_id
   if (N == 0) {
     // empty lists: zero counts and offsets
     hipStream_t s = (hipStream_t)stream;
-    if (hipMemsetAsync(counts, 0, sizeof(int32_t) * cfg->n_routed_experts, s) != hipSuccess) return MOE_ERR_HIP;
-    if (hipMemsetAsync(offsets, 0, sizeof(int32_t) * (cfg->n_routed_experts + 1), s) != hipSuccess)
-      return MOE_ERR_HIP;
+    if (launch_fill_i32(counts, cfg->n_routed_experts, 0, s) != hipSuccess) return MOE_ERR_HIP;
+    if (launch_fill_i32(offsets, cfg->n_routed_experts + 1, 0, s) != hipSuccess) return MOE_ERR_HIP;
     return MOE_OK;
   }
   return dispatch_impl(cfg, N, topk_idx, counts, offsets, sorted_pair, inv_row, workspace, L, (hipStream_t)stream);
@@ -238,65 +288,57 @@ moe_status moe_forward(const moe_config* cfg, int64_t N, const void* x, const mo
   if (st != MOE_OK) return st;
   if ((st = check_n(cfg, N)) != MOE_OK) return st;
   if (!wt) return MOE_ERR_INVALID_ARG;
-  const bool shared = cfg->n_shared_experts > 0;
   if (N == 0) return MOE_OK;
-  if (!x || !y || !wt->w_router || !wt->e_bias || !wt->gate_up || !wt->down) return MOE_ERR_INVALID_ARG;
-  if (shared && (!wt->sh_gate || !wt->sh_up || !wt->sh_down)) return MOE_ERR_INVALID_ARG;
-  if (!aligned16(x) || !aligned16(y) || !aligned16(wt->w_router) || !aligned16(wt->gate_up) || !aligned16(wt->down))
-    return MOE_ERR_INVALID_ARG;
-  if (shared && (!aligned16(wt->sh_gate) || !aligned16(wt->sh_up) || !aligned16(wt->sh_down)))
-    return MOE_ERR_INVALID_ARG;
-  if (x == y) return MOE_ERR_INVALID_ARG;
+  if ((st = check_expert_args(cfg, x, wt, y)) != MOE_OK) return st;
+  if (!wt->w_router || !wt->e_bias || !aligned16(wt->w_router)) return MOE_ERR_INVALID_ARG;
   const Workspace L = layout(cfg, N);
   if (!workspace || ws_bytes < L.total || !aligned16(workspace)) return MOE_ERR_WORKSPACE;
 
   hipStream_t s = (hipStream_t)stream;
   void* ws = workspace;
-  const int E = cfg->n_routed_experts, k = cfg->num_experts_per_tok, D = cfg->hidden_size;
-  const int d = cfg->moe_intermediate_size, dsh = d * cfg->n_shared_experts;
-  const int64_t es = cfg->dtype == MOE_F32 ? 4 : 2;
-
+  const int E = cfg->n_routed_experts, k = cfg->num_experts_per_tok;
   int32_t* idx = at<int32_t>(ws, L.idx);
   float* w = at<float>(ws, L.w);
   int32_t* counts = at<int32_t>(ws, L.counts);
-  int32_t* sorted_pair = at<int32_t>(ws, L.sorted_pair);
-  int32_t* inv_row = at<int32_t>(ws, L.inv_row);
 
   if ((st = route_impl(cfg, N, x, wt->w_router, wt->e_bias, at<float>(ws, L.scores), 0, idx, w, ws, L, s)) != MOE_OK)
     return st;
-  if ((st = dispatch_impl(cfg, N, idx, counts, at<int32_t>(ws, L.offsets), sorted_pair, inv_row, ws, L, s)) != MOE_OK)
+  if ((st = dispatch_impl(cfg, N, idx, counts, at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.sorted_pair),
+                          at<int32_t>(ws, L.inv_row), ws, L, s)) != MOE_OK)
     return st;
-
-  GroupedArgs g{};
-  g.sorted_pair = sorted_pair;
-  g.topk_w = w;
-  g.k = k;
-  g.offsets = at<int32_t>(ws, L.offsets);
-  // gate_up + SwiGLU: routed rows gather x through sorted_pair; the shared expert reads x in order
-  g.tiles = at<Tile>(ws, L.tiles0);
-  g.n_tiles = at<int32_t>(ws, L.ntiles);
-  g.bm = L.bm0;
-  g.prob[0] = ExpertProblem{x, D, 1, wt->gate_up, (const char*)wt->gate_up + es * (int64_t)d * D, 2LL * d * D, D, d,
-                            at<void>(ws, L.H), d, 0};
-  if (shared)
-    g.prob[1] = ExpertProblem{x, D, 0, wt->sh_gate, wt->sh_up, 0, D, dsh, at<void>(ws, L.Hsh), dsh, 0};
-  MOE_TRY(ST_GATE_UP, launch_gate_up(cfg->dtype, g, L.max_tiles0, s));
-  // down + mixture weight (routed) / weight 1 (shared)
-  g.tiles = at<Tile>(ws, L.tiles1);
-  g.n_tiles = at<int32_t>(ws, L.ntiles) + 1;
-  g.bm = L.bm1;
-  g.prob[0] = ExpertProblem{at<void>(ws, L.H), d, 0, wt->down, nullptr, (int64_t)D * d, d, D, at<void>(ws, L.Y), D, 1};
-  if (shared)
-    g.prob[1] = ExpertProblem{at<void>(ws, L.Hsh), dsh, 0, wt->sh_down, nullptr, 0, dsh, D, at<void>(ws, L.Ysh), D, 0};
-  MOE_TRY(ST_DOWN, launch_down(cfg->dtype, g, L.max_tiles1, s));
-  MOE_TRY(ST_COMBINE, launch_combine(cfg->dtype, at<void>(ws, L.Y), shared ? at<void>(ws, L.Ysh) : nullptr, inv_row, N,
-                                     k, D, y, s));
+  if ((st = experts_impl(cfg, N, x, wt, w, y, ws, L, s)) != MOE_OK) return st;
 
   if (topk_idx_out && hipMemcpyAsync(topk_idx_out, idx, sizeof(int32_t) * N * k, hipMemcpyDeviceToDevice, s))
     return MOE_ERR_HIP;
   if (topk_w_out && hipMemcpyAsync(topk_w_out, w, sizeof(float) * N * k, hipMemcpyDeviceToDevice, s))
     return MOE_ERR_HIP;
   if (counts_out && hipMemcpyAsync(counts_out, counts, sizeof(int32_t) * E, hipMemcpyDeviceToDevice, s))
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+moe_status moe_forward_routed(const moe_config* cfg, int64_t N, const void* x, const moe_weights* wt,
+                              const int32_t* topk_idx, const float* topk_w, void* y, int32_t* counts_out,
+                              void* workspace, size_t ws_bytes, void* stream) {
+  moe_status st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if ((st = check_n(cfg, N)) != MOE_OK) return st;
+  if (!wt) return MOE_ERR_INVALID_ARG;
+  if (N == 0) return MOE_OK;
+  if ((st = check_expert_args(cfg, x, wt, y)) != MOE_OK) return st;
+  if (!topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
+  const Workspace L = layout(cfg, N);
+  if (!workspace || ws_bytes < L.total || !aligned16(workspace)) return MOE_ERR_WORKSPACE;
+
+  hipStream_t s = (hipStream_t)stream;
+  void* ws = workspace;
+  int32_t* counts = at<int32_t>(ws, L.counts);
+  if ((st = dispatch_impl(cfg, N, topk_idx, counts, at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.sorted_pair),
+                          at<int32_t>(ws, L.inv_row), ws, L, s)) != MOE_OK)
+    return st;
+  if ((st = experts_impl(cfg, N, x, wt, topk_w, y, ws, L, s)) != MOE_OK) return st;
+  if (counts_out && hipMemcpyAsync(counts_out, counts, sizeof(int32_t) * cfg->n_routed_experts,
+                                   hipMemcpyDeviceToDevice, s))
     return MOE_ERR_HIP;
   return MOE_OK;
 }

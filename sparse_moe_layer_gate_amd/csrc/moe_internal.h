@@ -41,8 +41,15 @@ __device__ inline uint16_t bf16_rne(float f) {
 }
 __device__ inline float bf16_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-// SwiGLU of one intermediate column: silu(gate) * up.
-__device__ inline float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+// SwiGLU of one intermediate column: SiLU(gate) * up, clamped first when lim > 0 (gate from above only,
+// up on both sides: "Module 02 -- MoE: Capacity, Work, and Traffic", section 3).
+__device__ inline float swiglu(float g, float u, float lim) {
+  if (lim > 0.f) {
+    g = fminf(g, lim);
+    u = fminf(fmaxf(u, -lim), lim);
+  }
+  return g / (1.0f + expf(-g)) * u;
+}
 
 // s_waitcnt with vmcnt = N and the other counters left at their maximum (gfx9 encoding).
 template <int N>
@@ -107,6 +114,7 @@ struct GroupedArgs {
   const float* topk_w;
   int k;
   const int32_t* offsets;  // routed experts' row offsets [E + 1] (or nullptr: every expert counts as large)
+  float swiglu_limit;      // gate_up epilogue clamp bound (0: plain SwiGLU)
 };
 // Field-wise select keeps a problem descriptor in scalar registers (a dynamically indexed
 // kernel-argument array would be copied to scratch).
@@ -150,7 +158,10 @@ hipError_t launch_bf16_prefill(bool gate_up, int bm, const GroupedArgs& a, int64
 hipError_t launch_bf16_decode(bool gate_up, const GroupedArgs& a, int64_t max_tile_count, hipStream_t s);
 
 // ---- combine ----
+// y = alpha_out * (routed rows in slot order) + shared row
 hipError_t launch_combine(int dtype, const void* Y, const void* Ysh, const int32_t* inv_row, int64_t N, int k, int D,
-                          void* y, hipStream_t s);
+                          float alpha_out, void* y, hipStream_t s);
+// p[0 .. n) = v (a kernel rather than a memset node, so the call may sit in a captured graph)
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
 
 }  // namespace moe

@@ -96,6 +96,24 @@ def gpu_forward(w: synth.Workload, x_dev, dev_w: dict):
     return out
 
 
+def gpu_forward_routed(w: synth.Workload, x_dev, dev_w: dict, idx: np.ndarray, wt: np.ndarray):
+    """moe_forward_routed through the C ABI with host routing (idx, wt); returns (y, counts) as host arrays."""
+    import sparse_moe_layer_gate_amd as moe
+
+    torch = torch_mod()
+    cfg = moe.config_of(w)
+    N = x_dev.shape[0]
+    ws = moe.alloc_workspace(cfg, N)
+    y = torch.empty_like(x_dev)
+    counts = torch.empty((w.E,), dtype=torch.int32, device="cuda")
+    moe.moe_forward_routed(cfg, N, x_dev, dev_w, to_device(np.ascontiguousarray(idx, np.int32)),
+                           to_device(np.ascontiguousarray(wt, np.float32)), y, ws, counts)
+    torch.cuda.synchronize()
+    out = to_host(y), to_host(counts)
+    del ws, y
+    return out
+
+
 def score_tolerance(w: synth.Workload, x: np.ndarray, wg: np.ndarray) -> np.ndarray:
     """Per-element bound on |s_gpu - s_oracle|. The device logit is a float32 accumulation of at most 3 D
     exact products (bf16 activations times the three bf16 pieces of the router weight; D products for
@@ -137,3 +155,37 @@ def isclose_ulps(a, b, n):
 
 def std_of(fan_in):
     return 1.0 / math.sqrt(fan_in)
+
+
+def check_forward(w, x, wg, b, y, idx, wt, counts, tokens):
+    """Routing check over all tokens, output check over `tokens`."""
+    s_ref = oracle.scores(w, x, wg)
+    idx_ref, w_ref = oracle.select(w, s_ref, b)
+    margin = oracle.select_margin(w, s_ref, b)
+    tol_s = score_tolerance(w, x, wg).max(axis=1)
+    differ = np.any(idx != idx_ref, axis=1)
+    assert np.all(margin[differ] <= 2 * tol_s[differ]), "a routing difference away from a near-tie"
+    assert np.array_equal(counts, np.bincount(idx.ravel(), minlength=w.E))
+    same = ~differ
+    # weights from the GPU's own scores: the score bound t propagated through w_i = alpha s_i / S,
+    # |dw_i| <= alpha (t / S + s_i k t / S^2), plus 4 ulp of the float32 steps
+    chosen = np.take_along_axis(s_ref, idx_ref.astype(np.int64), 1).astype(np.float64)
+    aw = 1.0 if w.alpha_on_output else w.alpha  # the factor the weights carry
+    if w.norm:
+        S = chosen.sum(axis=1, keepdims=True) + w.eps
+        bound = aw * (tol_s[:, None] / S + chosen * w.k * tol_s[:, None] / S**2)
+    else:
+        bound = aw * tol_s[:, None] * np.ones_like(chosen)
+    bound = bound + 4 * np.spacing(np.abs(w_ref).astype(np.float32))
+    dev_w = np.abs(wt.astype(np.float64) - w_ref)
+    assert np.all(dev_w[same] <= bound[same]), f"weight deviation {dev_w[same].max():.3g}"
+    # per-token reference: the oracle's routing, or the GPU's where they differ at a near-tie
+    tokens = np.unique(np.concatenate([tokens, np.flatnonzero(differ)[:8]]))
+    r_idx = np.where(differ[:, None], idx, idx_ref)
+    r_w = np.where(differ[:, None], wt, w_ref)
+    table = expert_table(w, r_idx[tokens].ravel())
+    y_ref = oracle.forward_tokens(w, tokens, x, table, r_idx, r_w)
+    err = rel_err(as_f32(y[tokens]), y_ref)
+    print(f"  {w.name}: tokens={tokens.size} differ={int(differ.sum())} rel_err={err:.3g}", flush=True)
+    assert err <= TOL[w.dtype], err
+    return err

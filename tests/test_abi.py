@@ -56,12 +56,40 @@ def test_workspace_size_small_and_monotone():
     ("eps", -1.0, moe.MOE_ERR_INVALID_ARG),
     ("D", 200, moe.MOE_ERR_UNSUPPORTED),    # not a multiple of 64
     ("d", 96, moe.MOE_ERR_UNSUPPORTED),
+    ("limit", -1.0, moe.MOE_ERR_INVALID_ARG),          # the SwiGLU bound is >= 0
+    ("limit", float("inf"), moe.MOE_ERR_INVALID_ARG),
+    ("limit", float("nan"), moe.MOE_ERR_INVALID_ARG),
 ])
 def test_config_errors(field, value, status):
     w = replace(synth.WORKLOADS["tiny_fp32"], **{field: value})
     cfg = moe.config_of(w)
     assert moe.moe_check_config(cfg) == status
     assert moe.moe_workspace_size(cfg, 10) == 0
+
+
+def test_alpha_placement_field():
+    base = synth.WORKLOADS["tiny_fp32"]
+    assert moe.moe_check_config(moe.config_of(replace(base, alpha_on_output=True))) == moe.MOE_OK
+    cfg = moe.config_of(base)
+    cfg.alpha_on_output = 2
+    assert moe.moe_check_config(cfg) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_routed_forward_argument_errors():
+    """moe_forward_routed: missing routing, x == y and short workspaces are host errors; N = 0 is a no-op."""
+    cfg = moe.config_of(synth.WORKLOADS["tiny_fp32"])
+    L = moe.lib()
+    fake = ctypes.c_void_p(4096)  # never dereferenced
+    ws = moe.MoeWeights(None, None, fake, fake, fake, fake, fake)  # no router weights needed
+    x, y = ctypes.c_void_p(8192), ctypes.c_void_p(12288)
+    assert L.moe_forward_routed(ctypes.byref(cfg), 4, x, ctypes.byref(ws), None, fake, y, None, fake, 1 << 30,
+                                None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_forward_routed(ctypes.byref(cfg), 4, x, ctypes.byref(ws), fake, fake, x, None, fake, 1 << 30,
+                                None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_forward_routed(ctypes.byref(cfg), 4, x, ctypes.byref(ws), fake, fake, y, None, fake, 16,
+                                None) == moe.MOE_ERR_WORKSPACE
+    assert L.moe_forward_routed(ctypes.byref(cfg), 0, None, ctypes.byref(ws), None, None, None, None, None, 0,
+                                None) == moe.MOE_OK
 
 
 def test_unsupported_limits():

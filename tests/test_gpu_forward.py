@@ -18,39 +18,6 @@ from tests import _harness as H
 pytestmark = pytest.mark.gpu
 
 
-def _check_forward(w, x, wg, b, y, idx, wt, counts, tokens, on_device_weights):
-    """Routing check over all tokens, output check over `tokens`."""
-    s_ref = oracle.scores(w, x, wg)
-    idx_ref, w_ref = oracle.select(w, s_ref, b)
-    margin = oracle.select_margin(w, s_ref, b)
-    tol_s = H.score_tolerance(w, x, wg).max(axis=1)
-    differ = np.any(idx != idx_ref, axis=1)
-    assert np.all(margin[differ] <= 2 * tol_s[differ]), "a routing difference away from a near-tie"
-    assert np.array_equal(counts, np.bincount(idx.ravel(), minlength=w.E))
-    same = ~differ
-    # weights from the GPU's own scores: the score bound t propagated through w_i = alpha s_i / S,
-    # |dw_i| <= alpha (t / S + s_i k t / S^2), plus 4 ulp of the float32 steps
-    chosen = np.take_along_axis(s_ref, idx_ref.astype(np.int64), 1).astype(np.float64)
-    if w.norm:
-        S = chosen.sum(axis=1, keepdims=True) + w.eps
-        bound = w.alpha * (tol_s[:, None] / S + chosen * w.k * tol_s[:, None] / S**2)
-    else:
-        bound = w.alpha * tol_s[:, None] * np.ones_like(chosen)
-    bound = bound + 4 * np.spacing(np.abs(w_ref).astype(np.float32))
-    dev_w = np.abs(wt.astype(np.float64) - w_ref)
-    assert np.all(dev_w[same] <= bound[same]), f"weight deviation {dev_w[same].max():.3g}"
-    # per-token reference: the oracle's routing, or the GPU's where they differ at a near-tie
-    tokens = np.unique(np.concatenate([tokens, np.flatnonzero(differ)[:8]]))
-    r_idx = np.where(differ[:, None], idx, idx_ref)
-    r_w = np.where(differ[:, None], wt, w_ref)
-    table = H.expert_table(w, r_idx[tokens].ravel())
-    y_ref = oracle.forward_tokens(w, tokens, x, table, r_idx, r_w)
-    err = H.rel_err(H.as_f32(y[tokens]), y_ref)
-    print(f"  {w.name}: tokens={tokens.size} differ={int(differ.sum())} rel_err={err:.3g}", flush=True)
-    assert err <= H.TOL[w.dtype], err
-    return err
-
-
 @pytest.mark.parametrize("name", synth.WORKLOAD_ORDER)
 def test_forward_workload(name):
     w = synth.WORKLOADS[name]
@@ -60,7 +27,7 @@ def test_forward_workload(name):
     x = synth.x_host(w)
     y, idx, wt, counts = H.gpu_forward(w, H.to_device(x), dev)
     tokens = H.sample_tokens(w.N, 24 if big else w.N, seed=1)
-    _check_forward(w, x, wg, b, y, idx, wt, counts, tokens, big)
+    H.check_forward(w, x, wg, b, y, idx, wt, counts, tokens)
 
 
 SMALL = [
@@ -85,7 +52,7 @@ def test_forward_small_whole(case, dtype):
     wg, b, dev = H.device_weights(w, generate_on_device=False)
     x = synth.x_host(w)
     y, idx, wt, counts = H.gpu_forward(w, H.to_device(x), dev)
-    _check_forward(w, x, wg, b, y, idx, wt, counts, np.arange(w.N), False)
+    H.check_forward(w, x, wg, b, y, idx, wt, counts, np.arange(w.N))
 
 
 def test_forward_deterministic_and_permutation_equivariant():
