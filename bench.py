@@ -240,6 +240,81 @@ def time_forward(w: synth.Workload, st: dict, steps: int, warmup: int) -> dict:
     return {"ms_per_step": (t1 - t0) * 1e3 / steps, "stages": stages, "counts": counts}
 
 
+def decode_sweep(w: synth.Workload, sizes: list, steps: int, warmup: int) -> list:
+    """Token-count sweep at a decode shape ("Module 02 -- MoE: Capacity, Work, and Traffic", sections 1 and
+    5: traffic, set by the distinct experts a batch touches, governs decode). Weights are generated once;
+    batch N takes the first N tokens of the workload's x stream. Per N: time per step, distinct experts,
+    collision rate (share of (token, slot) pairs whose expert another pair of the batch also uses), the
+    algorithmic bytes and the achieved HBM rate."""
+    import torch
+
+    import sparse_moe_layer_gate_amd as moe
+
+    wmax = w.with_tokens(max(sizes))
+    st = setup(wmax)
+    rows = []
+    for N in sizes:
+        wn = w.with_tokens(N)
+        sub = {**st, "cfg": moe.config_of(wn), "x": st["x"][:N].contiguous(), "y": st["y"][:N].contiguous(),
+               "ws": moe.alloc_workspace(moe.config_of(wn), N)}
+        r = time_forward(wn, sub, steps, warmup)
+        m = measure(wn, r)
+        distinct = m["layer"]["distinct_experts"]
+        by = m["layer"]["algorithmic_bytes"]
+        uniform = w.E * (1.0 - (1.0 - w.k / w.E) ** N)  # expected distinct experts under uniform routing
+        rows.append({"N": N, "ms_per_step": round(m["ms"], 4), "tokens_per_s": round(N / (m["ms"] * 1e-3), 1),
+                     "distinct_experts": distinct, "uniform_expectation": round(uniform, 1),
+                     "collision_rate": round(1.0 - distinct / (N * w.k), 4),
+                     "algorithmic_gb": round(by / 1e9, 3), "gb_per_s": round(by / (m["ms"] * 1e-3) / 1e9, 1),
+                     "hbm_frac": m["layer"]["hbm_frac"], "gate_up_ms": m["layer"]["stage_ms"].get(DOMINANT),
+                     "gate_up_hbm_frac": m["roofline"]["frac"] if m["roofline"]["bound"] == "hbm" else None})
+        print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
+        del sub
+    del st
+    torch.cuda.empty_cache()
+    return rows
+
+
+def dense_bench(w, steps: int, warmup: int) -> dict:
+    """The dense SwiGLU FFN (moe_dense_forward) at its full width: time per step, TFLOP/s and the MFMA
+    fraction of each GEMM (algorithmic work 6 N D dff: gate_up 4 N D dff, down 2 N D dff)."""
+    import torch
+
+    import sparse_moe_layer_gate_amd as moe
+
+    dev = synth.dense_device(w)
+    x = synth.x_host(w)
+    xd = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda() if x.dtype == np.uint16 else \
+        torch.from_numpy(x).cuda()
+    y = torch.empty_like(xd)
+    ws = torch.empty(moe.moe_dense_workspace_size(w.N, w.D, w.dff, w.dtype), dtype=torch.uint8, device="cuda")
+
+    def step():
+        moe.moe_dense_forward(w.N, xd, dev["gate"], dev["up"], dev["down"], y, ws, limit=w.limit)
+
+    for _ in range(warmup + 1):
+        step()
+    torch.cuda.synchronize()
+    moe.profile_begin()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stages = moe.profile_end()
+    ms = (t1 - t0) * 1e3 / steps
+    fl = 6.0 * w.N * w.D * w.dff
+    out = {"workload": w.name, "N": w.N, "D": w.D, "dff": w.dff, "ms_per_step": round(ms, 4),
+           "tokens_per_s": round(w.N / (ms * 1e-3), 1), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+           "mfma_frac": round(fl / (ms * 1e-3) / P_BF16, 4)}
+    for name, share in (("experts_gate_up", 4.0), ("experts_down", 2.0)):
+        t, n = stages[name]
+        avg = t / max(n, 1)
+        out[name.replace("experts_", "") + "_ms"] = round(avg, 4)
+        out[name.replace("experts_", "") + "_mfma_frac"] = round(share * w.N * w.D * w.dff / (avg * 1e-3) / P_BF16, 4)
+    return out
+
+
 def cpu_baseline(w: synth.Workload, tokens: int) -> dict:
     """The oracle (routing + per-expert loop form) on the first `tokens` tokens of the workload."""
     import oracle
@@ -277,6 +352,10 @@ def main():
                     help="only run a plain 1 GiB device copy (for scaling rocprofv3 byte counters)")
     ap.add_argument("--profile-summary", metavar="DIR",
                     help="summarise rocprofv3 output under DIR for --workload (no GPU needed) and exit")
+    ap.add_argument("--decode-sweep", action="store_true",
+                    help="time --workload (a decode shape) at N = 1, 2, 4, ..., 256 tokens and print a table")
+    ap.add_argument("--dense", choices=sorted(synth.DENSE_WORKLOADS),
+                    help="time the dense SwiGLU FFN of this shape instead of the MoE layer and print one JSON line")
     args = ap.parse_args()
     if args.profile_summary:
         w = synth.WORKLOADS[args.workload]
@@ -301,7 +380,20 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n, "launches": 3}))
         return
 
+    if args.dense:
+        print(json.dumps(dense_bench(synth.DENSE_WORKLOADS[args.dense], args.steps, args.warmup)), flush=True)
+        return
     w = synth.WORKLOADS[args.workload]
+    if args.decode_sweep:
+        rows = decode_sweep(w, [1 << i for i in range(9)], args.decode_steps, args.warmup)
+        keys = list(rows[0].keys())
+        print(f"decode sweep, {w.name} (D={w.D}, E={w.E}, G={w.G}, TG={w.TG}, k={w.k}, d={w.d}, "
+              f"n_shared={w.n_shared}), {args.decode_steps} steps per N\n")
+        print("| " + " | ".join(keys) + " |")
+        print("|" + "---|" * len(keys))
+        for r in rows:
+            print("| " + " | ".join(str(r[k]) for k in keys) + " |")
+        return
     print(f"[bench] {w.name}: generating inputs", file=sys.stderr, flush=True)
     st = setup(w)
     r = time_forward(w, st, args.steps, args.warmup)

@@ -161,6 +161,20 @@ moe_status moe_forward_routed(const moe_config* cfg, int64_t N, const void* x, c
                               const int32_t* topk_idx, const float* topk_w, void* y, int32_t* counts_out,
                               void* workspace, size_t ws_bytes, void* stream);
 
+/* The dense SwiGLU FFN of the layers before the MoE ones ("Shared output" (GLM-5), the evidence from the
+ * shared expert: the dense feed-forward network is the same bias-free SwiGLU MLP,
+ * y = W_down (SiLU(W_gate x) * W_up x), at the model's full intermediate width; "MoE Forward": dense
+ * prefix layers never enter the MoE module). Runs on the same GEMM kernels as the shared expert.
+ *   N, D, dff: tokens, hidden size, intermediate width (D and dff multiples of 64)
+ *   dtype: moe_dtype of x, the weights and y; swiglu_limit as in moe_config (0: plain SwiGLU)
+ *   x [N, D], gate [dff, D], up [dff, D], down [D, dff], y [N, D] (y must not overlap x)
+ *   workspace, ws_bytes: at least moe_dense_workspace_size(N, D, dff, dtype) bytes.
+ * Errors as for the other calls; N = 0 launches nothing. */
+size_t moe_dense_workspace_size(int64_t N, int32_t D, int32_t dff, int32_t dtype);
+moe_status moe_dense_forward(int64_t N, int32_t D, int32_t dff, int32_t dtype, float swiglu_limit, const void* x,
+                             const void* gate, const void* up, const void* down, void* y, void* workspace,
+                             size_t ws_bytes, void* stream);
+
 /* Static string naming a status. */
 const char* moe_status_str(moe_status status);
 

@@ -19,8 +19,8 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_ROUTE_SCORES_IN = 1
 
 EXPORTED = ["moe_check_config", "moe_workspace_size", "moe_route", "moe_dispatch", "moe_forward",
-            "moe_forward_routed", "moe_status_str", "moe_profile_begin", "moe_profile_end", "moe_stage_name",
-            "moe_stage_count"]
+            "moe_forward_routed", "moe_dense_workspace_size", "moe_dense_forward", "moe_status_str",
+            "moe_profile_begin", "moe_profile_end", "moe_stage_name", "moe_stage_count"]
 
 
 class MoeError(RuntimeError):
@@ -74,6 +74,10 @@ def lib():
         L.moe_forward.argtypes = [cp, i64, vp, ctypes.POINTER(MoeWeights), vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.moe_forward_routed.argtypes = [cp, i64, vp, ctypes.POINTER(MoeWeights), vp, vp, vp, vp, vp,
                                          ctypes.c_size_t, vp]
+        L.moe_dense_workspace_size.argtypes = [i64, i32, i32, i32]
+        L.moe_dense_workspace_size.restype = ctypes.c_size_t
+        L.moe_dense_forward.argtypes = [i64, i32, i32, i32, ctypes.c_float, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                        vp]
         L.moe_forward.restype = ctypes.c_int
         L.moe_status_str.argtypes = [ctypes.c_int]
         L.moe_status_str.restype = ctypes.c_char_p
@@ -267,6 +271,29 @@ def moe_forward_routed(cfg: MoeConfig, N: int, x, weights, topk_idx, topk_w, y, 
         workspace.numel(),
         _stream(stream))
     _check(st, "moe_forward_routed")
+
+
+def _dtype_code(dtype) -> int:
+    return {"bf16": MOE_BF16, "f32": MOE_F32}[dtype] if isinstance(dtype, str) else int(dtype)
+
+
+def moe_dense_workspace_size(N: int, D: int, dff: int, dtype="bf16") -> int:
+    return int(lib().moe_dense_workspace_size(int(N), int(D), int(dff), _dtype_code(dtype)))
+
+
+def moe_dense_forward(N: int, x, gate, up, down, y, workspace, limit: float = 0.0, stream=None):
+    """Dense SwiGLU FFN y = down (SiLU(gate x) * up x); gate, up [dff, D], down [D, dff]."""
+    import torch
+
+    dff, D = gate.shape
+    dt = _dtype_code("f32" if x.dtype == torch.float32 else "bf16")
+    adt = torch.float32 if dt == MOE_F32 else torch.bfloat16
+    st = lib().moe_dense_forward(
+        int(N), int(D), int(dff), dt, float(limit),
+        _ptr(x, "x", adt, (N, D)), _ptr(gate, "gate", adt, (dff, D)), _ptr(up, "up", adt, (dff, D)),
+        _ptr(down, "down", adt, (D, dff)), _ptr(y, "y", adt, (N, D)),
+        _ptr(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream))
+    _check(st, "moe_dense_forward")
 
 
 def stage_names() -> list:

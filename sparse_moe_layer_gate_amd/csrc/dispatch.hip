@@ -161,6 +161,23 @@ __global__ __launch_bounds__(256) void place_kernel(const int32_t* __restrict__ 
   }
 }
 
+// Tile lists of one dense problem (problem 0, expert 0) over N rows, for the dense FFN.
+__global__ __launch_bounds__(256) void dense_tiles_kernel(int64_t N, TileSpec t0, TileSpec t1) {
+  for (int which = 0; which < 2; ++which) {
+    const TileSpec& ts = which ? t1 : t0;
+    const int64_t nt = (N + ts.bm - 1) / ts.bm;
+    for (int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x; j < nt; j += (int64_t)gridDim.x * 256) {
+      Tile t;
+      t.problem = 0;
+      t.expert = 0;
+      t.row_start = (int)(j * ts.bm);
+      t.rows = (int)min((int64_t)ts.bm, N - j * ts.bm);
+      ts.tiles[j] = t;
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) *ts.n_tiles = (int)nt;
+  }
+}
+
 __global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* __restrict__ p, int64_t n, int32_t v) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = v;
 }
@@ -171,6 +188,13 @@ hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   const int64_t blocks = min((n + 255) / 256, (int64_t)1024);
   hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_tiles(int64_t N, TileSpec t0, TileSpec t1, hipStream_t s) {
+  const int64_t nt = (N + min(t0.bm, t1.bm) - 1) / min(t0.bm, t1.bm);
+  const int64_t blocks = max((int64_t)1, min((nt + 255) / 256, (int64_t)256));
+  hipLaunchKernelGGL(dense_tiles_kernel, dim3((unsigned)blocks), dim3(256), 0, s, N, t0, t1);
   return hipGetLastError();
 }
 

@@ -94,6 +94,41 @@ Workspace layout(const moe_config* c, int64_t N) {
   return w;
 }
 
+// Dense FFN workspace: tile lists and the intermediate H [N, dff].
+struct DenseWorkspace {
+  size_t tiles0, tiles1, ntiles, H, total;
+  int bm;
+  int64_t max_tiles;
+};
+
+DenseWorkspace dense_layout(int64_t N, int dff, int dtype) {
+  DenseWorkspace w{};
+  const int64_t es = dtype == MOE_F32 ? 4 : 2;
+  w.bm = gemm_bm(dtype, N, 1, 1);
+  w.max_tiles = (N + w.bm - 1) / w.bm;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  w.tiles0 = take(sizeof(Tile) * w.max_tiles);
+  w.tiles1 = take(sizeof(Tile) * w.max_tiles);
+  w.ntiles = take(sizeof(int32_t) * 2);
+  w.H = take(es * N * dff);
+  w.total = o;
+  return w;
+}
+
+moe_status check_dense(int64_t N, int32_t D, int32_t dff, int32_t dtype, float limit) {
+  if (N < 0 || D < 1 || dff < 1) return MOE_ERR_INVALID_ARG;
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (!std::isfinite(limit) || limit < 0.f) return MOE_ERR_INVALID_ARG;
+  if (D % 64 != 0 || dff % 64 != 0 || dff > (1 << 24)) return MOE_ERR_UNSUPPORTED;
+  if (N >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
 template <typename T>
 T* at(void* ws, size_t off) {
   return (T*)((char*)ws + off);
@@ -340,6 +375,45 @@ moe_status moe_forward_routed(const moe_config* cfg, int64_t N, const void* x, c
   if (counts_out && hipMemcpyAsync(counts_out, counts, sizeof(int32_t) * cfg->n_routed_experts,
                                    hipMemcpyDeviceToDevice, s))
     return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+size_t moe_dense_workspace_size(int64_t N, int32_t D, int32_t dff, int32_t dtype) {
+  if (check_dense(N, D, dff, dtype, 0.f) != MOE_OK) return 0;
+  return dense_layout(N, dff, dtype).total;
+}
+
+moe_status moe_dense_forward(int64_t N, int32_t D, int32_t dff, int32_t dtype, float swiglu_limit, const void* x,
+                             const void* gate, const void* up, const void* down, void* y, void* workspace,
+                             size_t ws_bytes, void* stream) {
+  moe_status st = check_dense(N, D, dff, dtype, swiglu_limit);
+  if (st != MOE_OK) return st;
+  if (N == 0) return MOE_OK;
+  if (!x || !gate || !up || !down || !y || x == y) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(gate) || !aligned16(up) || !aligned16(down) || !aligned16(y))
+    return MOE_ERR_INVALID_ARG;
+  const DenseWorkspace L = dense_layout(N, dff, dtype);
+  if (!workspace || ws_bytes < L.total || !aligned16(workspace)) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  void* ws = workspace;
+  int32_t* ntiles = at<int32_t>(ws, L.ntiles);
+  TileSpec t0{L.bm, at<Tile>(ws, L.tiles0), ntiles};
+  TileSpec t1{L.bm, at<Tile>(ws, L.tiles1), ntiles + 1};
+  if (launch_dense_tiles(N, t0, t1, s) != hipSuccess) return MOE_ERR_HIP;
+  // one dense problem through the grouped GEMMs: no gather, no row scale; offsets = nullptr marks it
+  // as a large problem for the prefill kernel's loop choice
+  GroupedArgs g{};
+  g.k = 1;
+  g.swiglu_limit = swiglu_limit;
+  g.tiles = t0.tiles;
+  g.n_tiles = ntiles;
+  g.bm = L.bm;
+  g.prob[0] = ExpertProblem{x, D, 0, gate, up, 0, D, dff, at<void>(ws, L.H), dff, 0};
+  MOE_TRY(ST_GATE_UP, launch_gate_up(dtype, g, L.max_tiles, s));
+  g.tiles = t1.tiles;
+  g.n_tiles = ntiles + 1;
+  g.prob[0] = ExpertProblem{at<void>(ws, L.H), dff, 0, down, nullptr, 0, dff, D, y, D, 0};
+  MOE_TRY(ST_DOWN, launch_down(dtype, g, L.max_tiles, s));
   return MOE_OK;
 }
 

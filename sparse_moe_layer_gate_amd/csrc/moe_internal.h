@@ -88,6 +88,8 @@ hipError_t launch_count(const int32_t* idx, int64_t N, int k, int E, int32_t* ch
 hipError_t launch_scan(const int32_t* chunk_counts, int nchunks, int64_t N, int k, int E, int n_shared_problem,
                        int32_t* counts, int32_t* offsets, int32_t* chunk_base, TileSpec t0, TileSpec t1,
                        hipStream_t s);
+// Tile lists of a single dense problem over N rows (the dense FFN).
+hipError_t launch_dense_tiles(int64_t N, TileSpec t0, TileSpec t1, hipStream_t s);
 hipError_t launch_place(const int32_t* idx, int64_t N, int k, int E, const int32_t* chunk_base, int32_t* sorted_pair,
                         int32_t* inv_row, hipStream_t s);
 

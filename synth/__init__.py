@@ -22,6 +22,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 
 # Tensor ids (the Philox key's second word).
 ID_X, ID_WG, ID_BIAS, ID_GATE_UP, ID_DOWN, ID_SH_GATE, ID_SH_UP, ID_SH_DOWN, ID_SKEW, ID_X_DECODE = range(1, 11)
+ID_DENSE_GATE, ID_DENSE_UP, ID_DENSE_DOWN = range(11, 14)
 
 
 @dataclass(frozen=True)
@@ -78,6 +79,32 @@ WORKLOADS = {
 }
 WORKLOAD_ORDER = ["tiny_fp32", "air_prefill", "glm45_prefill_skewed", "glm5_prefill", "glm5_decode",
                   "glm53_flash_decode", "glm53_flash_prefill"]
+
+
+
+@dataclass(frozen=True)
+class DenseWorkload:
+    """A dense SwiGLU FFN (the layers before the MoE ones) and its input recipe."""
+
+    name: str
+    N: int
+    D: int
+    dff: int  # intermediate width (not on the pages: chosen, see the design notes)
+    dtype: str = "bf16"
+    seed: int = 0
+    limit: float = 0.0
+    outlier_every: int = 0
+    outlier_scale: float = 32.0
+    x_id: int = ID_X
+
+    def with_tokens(self, N: int) -> "DenseWorkload":
+        return replace(self, N=N)
+
+
+DENSE_WORKLOADS = {
+    # GLM-4.5-shaped dense prefix FFN: hidden 5120, intermediate width 12288.
+    "glm45_dense_ffn": DenseWorkload("glm45_dense_ffn", N=8192, D=5120, dff=12288),
+}
 
 # ---------------------------------------------------------------------------------------------
 _host = None
@@ -221,6 +248,15 @@ def all_experts_host(w: Workload) -> tuple[np.ndarray, np.ndarray]:
     return gu, dn
 
 
+def dense_host(w: DenseWorkload):
+    """Dense FFN weights: (gate [dff, D], up [dff, D], down [D, dff]); gate/up ~ N(0, 1/D), down ~ N(0, 1/dff)."""
+    n = w.dff * w.D
+    g = normal(w.seed, ID_DENSE_GATE, 0, n, 1.0 / math.sqrt(w.D), w.dtype).reshape(w.dff, w.D)
+    u = normal(w.seed, ID_DENSE_UP, 0, n, 1.0 / math.sqrt(w.D), w.dtype).reshape(w.dff, w.D)
+    dn = normal(w.seed, ID_DENSE_DOWN, 0, n, 1.0 / math.sqrt(w.dff), w.dtype).reshape(w.D, w.dff)
+    return g, u, dn
+
+
 # ---------------------------------------------------------------------------------------------
 # Device fill (torch tensors in HBM), bit-identical to the host recipes above.
 
@@ -257,4 +293,18 @@ def experts_device(w: Workload, device="cuda") -> dict:
         _dev_fill(out["sh_gate"], w.seed, ID_SH_GATE, 0, 1.0 / math.sqrt(w.D))
         _dev_fill(out["sh_up"], w.seed, ID_SH_UP, 0, 1.0 / math.sqrt(w.D))
         _dev_fill(out["sh_down"], w.seed, ID_SH_DOWN, 0, 1.0 / math.sqrt(w.d_sh))
+    return out
+
+
+def dense_device(w: DenseWorkload, device="cuda") -> dict:
+    """Dense FFN weights generated directly in HBM: gate [dff, D], up [dff, D], down [D, dff]."""
+    import torch
+
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    out = {"gate": torch.empty((w.dff, w.D), dtype=dt, device=device),
+           "up": torch.empty((w.dff, w.D), dtype=dt, device=device),
+           "down": torch.empty((w.D, w.dff), dtype=dt, device=device)}
+    _dev_fill(out["gate"], w.seed, ID_DENSE_GATE, 0, 1.0 / math.sqrt(w.D))
+    _dev_fill(out["up"], w.seed, ID_DENSE_UP, 0, 1.0 / math.sqrt(w.D))
+    _dev_fill(out["down"], w.seed, ID_DENSE_DOWN, 0, 1.0 / math.sqrt(w.dff))
     return out

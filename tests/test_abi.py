@@ -135,3 +135,24 @@ def test_status_strings():
 def test_stage_names():
     names = moe.stage_names()
     assert "experts_gate_up" in names and "experts_down" in names and len(names) == len(set(names))
+
+
+def test_dense_sizes_and_errors():
+    """The dense FFN entry: workspace sizing and host-side argument errors (no device touched)."""
+    L = moe.lib()
+    sizes = [moe.moe_dense_workspace_size(n, 5120, 12288, "bf16") for n in (0, 1, 47, 48, 383, 384, 8192)]
+    assert all(a <= b for a, b in zip(sizes, sizes[1:])) and sizes[-1] >= 8192 * 12288 * 2
+    assert moe.moe_dense_workspace_size(10, 200, 128, "bf16") == 0  # D not a multiple of 64
+    assert moe.moe_dense_workspace_size(-1, 256, 128, "bf16") == 0
+    fake = ctypes.c_void_p(4096)  # never dereferenced
+    x, y = ctypes.c_void_p(8192), ctypes.c_void_p(12288)
+    assert L.moe_dense_forward(4, 256, 128, moe.MOE_BF16, ctypes.c_float(0.0), x, fake, fake, fake, x, fake, 1 << 30,
+                               None) == moe.MOE_ERR_INVALID_ARG  # y == x
+    assert L.moe_dense_forward(4, 256, 128, moe.MOE_BF16, ctypes.c_float(-1.0), x, fake, fake, fake, y, fake,
+                               1 << 30, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_dense_forward(4, 256, 96, moe.MOE_BF16, ctypes.c_float(0.0), x, fake, fake, fake, y, fake, 1 << 30,
+                               None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_dense_forward(4, 256, 128, moe.MOE_BF16, ctypes.c_float(0.0), x, fake, fake, fake, y, fake, 16,
+                               None) == moe.MOE_ERR_WORKSPACE
+    assert L.moe_dense_forward(0, 256, 128, moe.MOE_BF16, ctypes.c_float(0.0), None, None, None, None, None, None, 0,
+                               None) == moe.MOE_OK
