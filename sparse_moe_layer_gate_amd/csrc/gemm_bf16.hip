@@ -19,8 +19,12 @@
 namespace moe {
 namespace {
 
-#ifndef MOE_PF_GROUP_ROWS
-#define MOE_PF_GROUP_ROWS 4
+// Rasterization: row tiles per column sweep (see grouped_bf16_lds), for gate_up and down.
+#ifndef MOE_PF_GROUP_ROWS_GU
+#define MOE_PF_GROUP_ROWS_GU 32
+#endif
+#ifndef MOE_PF_GROUP_ROWS_DN
+#define MOE_PF_GROUP_ROWS_DN 16
 #endif
 // L2 line touches ahead of the ring (see PrefillTile::TOUCH): distance in K steps (0: off) for the
 // gate_up and down GEMMs, the smallest routed-expert row count that turns them on, and which operands
@@ -209,7 +213,7 @@ __global__ __launch_bounds__(256, 1) void grouped_bf16_lds(GroupedArgs a, int nc
   const int64_t n_tiles = *a.n_tiles;
   const int64_t L = xcd_logical_block(n_tiles * ncol_max);
   if (L < 0) return;
-  constexpr int GR = MOE_PF_GROUP_ROWS;
+  constexpr int GR = GATE_UP ? MOE_PF_GROUP_ROWS_GU : MOE_PF_GROUP_ROWS_DN;
   const int64_t sg = L / ((int64_t)GR * ncol_max), within = L % ((int64_t)GR * ncol_max);
   // the last group may hold fewer than GR row tiles
   const int64_t gr = min((int64_t)GR, n_tiles - sg * GR);
@@ -351,9 +355,6 @@ __global__ __launch_bounds__(256, 1) void grouped_bf16_lds(GroupedArgs a, int nc
 
 #ifndef MOE_PF_BK
 #define MOE_PF_BK 64
-#endif
-#ifndef MOE_PF_GROUP_ROWS
-#define MOE_PF_GROUP_ROWS 4
 #endif
 #ifndef MOE_PF_STAGES
 #define MOE_PF_STAGES 2
