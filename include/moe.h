@@ -184,6 +184,9 @@ const char* moe_status_str(moe_status status);
  * (up to n_stages entries, indexed as moe_stage_name lists them) and stops recording. Returns
  * MOE_ERR_HIP if event creation or timing fails. Not thread-safe; for measurement only. */
 moe_status moe_profile_begin(void);
+/* As moe_profile_begin, recording only the stages whose bit (1 << stage) is set in stage_mask (fewer
+ * events in the stream when only some kernels are to be timed). */
+moe_status moe_profile_begin_mask(uint32_t stage_mask);
 moe_status moe_profile_end(double* ms_per_stage, int32_t* launches_per_stage, int32_t n_stages);
 /* Name of stage i (NULL past the last), and the number of stages. */
 const char* moe_stage_name(int32_t stage);

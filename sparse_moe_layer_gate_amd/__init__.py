@@ -20,7 +20,7 @@ MOE_ROUTE_SCORES_IN = 1
 
 EXPORTED = ["moe_check_config", "moe_workspace_size", "moe_route", "moe_dispatch", "moe_forward",
             "moe_forward_routed", "moe_dense_workspace_size", "moe_dense_forward", "moe_status_str",
-            "moe_profile_begin", "moe_profile_end", "moe_stage_name", "moe_stage_count"]
+            "moe_profile_begin", "moe_profile_begin_mask", "moe_profile_end", "moe_stage_name", "moe_stage_count"]
 
 
 class MoeError(RuntimeError):
@@ -82,6 +82,7 @@ def lib():
         L.moe_status_str.argtypes = [ctypes.c_int]
         L.moe_status_str.restype = ctypes.c_char_p
         L.moe_profile_begin.argtypes = []
+        L.moe_profile_begin_mask.argtypes = [u32]
         L.moe_profile_begin.restype = ctypes.c_int
         L.moe_profile_end.argtypes = [vp, vp, i32]
         L.moe_profile_end.restype = ctypes.c_int
@@ -301,8 +302,16 @@ def stage_names() -> list:
     return [L.moe_stage_name(i).decode() for i in range(L.moe_stage_count())]
 
 
-def profile_begin() -> None:
-    _check(lib().moe_profile_begin(), "moe_profile_begin")
+def profile_begin(stages=None) -> None:
+    """Start per-stage timing; `stages` (stage names) limits it to those stages."""
+    if stages is None:
+        _check(lib().moe_profile_begin(), "moe_profile_begin")
+        return
+    names = stage_names()
+    mask = 0
+    for st in stages:
+        mask |= 1 << names.index(st)
+    _check(lib().moe_profile_begin_mask(mask), "moe_profile_begin_mask")
 
 
 def profile_end() -> dict:

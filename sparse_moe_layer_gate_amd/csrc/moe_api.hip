@@ -140,6 +140,7 @@ struct ProfRec {
   hipEvent_t a, b;
 };
 bool g_prof_on = false;
+uint32_t g_prof_mask = 0;  // bit i: record stage i
 bool g_prof_err = false;
 std::vector<ProfRec> g_recs;
 std::vector<hipEvent_t> g_pool;
@@ -254,7 +255,7 @@ moe_status check_expert_args(const moe_config* cfg, const void* x, const moe_wei
 namespace moe {
 
 void prof_before(int stage, hipStream_t s) {
-  if (!g_prof_on) return;
+  if (!g_prof_on || !((g_prof_mask >> stage) & 1u)) return;
   ProfRec r{stage, next_event(), next_event()};
   if (!r.a || !r.b || hipEventRecord(r.a, s) != hipSuccess) {
     g_prof_err = true;
@@ -428,7 +429,10 @@ const char* moe_status_str(moe_status status) {
   return "unknown moe_status";
 }
 
-moe_status moe_profile_begin(void) {
+moe_status moe_profile_begin(void) { return moe_profile_begin_mask(~0u); }
+
+moe_status moe_profile_begin_mask(uint32_t stage_mask) {
+  g_prof_mask = stage_mask;
   g_recs.clear();
   g_pool_next = 0;
   g_prof_err = false;
