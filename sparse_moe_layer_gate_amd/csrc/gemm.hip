@@ -138,10 +138,14 @@ int64_t max_tiles(int64_t N, int k, int E, int n_shared_problem, int bm) {
   return routed + shared;
 }
 
+#ifndef MOE_BM256_ROWS
+#define MOE_BM256_ROWS 64  // average rows per expert from which the prefill GEMMs use 256-row tiles
+#endif
+
 int gemm_bm(int dtype, int64_t N, int k, int E) {
   if (dtype == MOE_F32) return F_BM;
   if (N * k < 48LL * E) return 16;           // weight-streaming decode kernel, 16-row tiles
-  return N * k >= 384LL * E ? 256 : 128;     // 256-row tiles when experts average 384+ rows
+  return N * k >= (int64_t)MOE_BM256_ROWS * E ? 256 : 128;  // 256-row tiles for row-heavy experts
 }
 
 hipError_t launch_gate_up(int dtype, const GroupedArgs& a, int64_t max_tile_count, hipStream_t s) {

@@ -183,3 +183,27 @@ def test_zero_tokens_is_noop():
     torch.cuda.synchronize()
     assert int(counts.abs().sum()) == 0 and int(offsets.abs().sum()) == 0
     del e
+
+
+def test_profile_stage_mask():
+    """Per-stage timing records every launched stage, or only the stages of the mask."""
+    import torch
+
+    import sparse_moe_layer_gate_amd as moe
+    from tests import _harness as H
+
+    w = synth.WORKLOADS["tiny_fp32"]
+    _, _, dev = H.device_weights(w, generate_on_device=False)
+    x = H.to_device(synth.x_host(w))
+    cfg = moe.config_of(w)
+    ws = moe.alloc_workspace(cfg, w.N)
+    y = torch.empty_like(x)
+    moe.profile_begin()
+    moe.moe_forward(cfg, w.N, x, dev, y, ws)
+    every = moe.profile_end()
+    moe.profile_begin(["experts_gate_up"])
+    moe.moe_forward(cfg, w.N, x, dev, y, ws)
+    only = moe.profile_end()
+    assert every["experts_gate_up"][1] == 1 and every["combine"][1] == 1 and every["router_select"][1] == 1
+    assert only["experts_gate_up"][1] == 1 and only["experts_gate_up"][0] > 0
+    assert all(n == 0 for name, (_, n) in only.items() if name != "experts_gate_up")
