@@ -138,13 +138,16 @@ int64_t max_tiles(int64_t N, int k, int E, int n_shared_problem, int bm) {
   return routed + shared;
 }
 
+#ifndef MOE_DECODE_ROWS
+#define MOE_DECODE_ROWS 12  // average rows per expert below which the decode kernels run
+#endif
 #ifndef MOE_BM256_ROWS
 #define MOE_BM256_ROWS 64  // average rows per expert from which the prefill GEMMs use 256-row tiles
 #endif
 
 int gemm_bm(int dtype, int64_t N, int k, int E) {
   if (dtype == MOE_F32) return F_BM;
-  if (N * k < 48LL * E) return 16;           // weight-streaming decode kernel, 16-row tiles
+  if (N * k < (int64_t)MOE_DECODE_ROWS * E) return 16;  // weight-streaming decode kernel, 16-row tiles
   return N * k >= (int64_t)MOE_BM256_ROWS * E ? 256 : 128;  // 256-row tiles for row-heavy experts
 }
 
