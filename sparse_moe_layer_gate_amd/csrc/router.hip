@@ -223,6 +223,7 @@ constexpr int SEL_MAX_KS = 16;  // logit partials per score (router_plan keeps K
 
 __device__ inline bool beats(float av, int ai, float bv, int bi) { return av > bv || (av == bv && ai < bi); }
 
+template <int MAXKS>
 __global__ __launch_bounds__(256) void select_kernel(float* __restrict__ scores, const float* __restrict__ part,
                                                      int KS, const float* __restrict__ bias, int64_t N, int E, int G,
                                                      int TG, int k, float alpha, int norm, float eps,
@@ -242,25 +243,47 @@ __global__ __launch_bounds__(256) void select_kernel(float* __restrict__ scores,
 
   float sp[SEL_MAX_P];
   bool elig[SEL_MAX_P];
+  float sraw[SEL_MAX_P];
+  // Scores: with partials, the KS partials of SEL_PB experts per lane are all loaded before the first
+  // add (one memory round trip per group of SEL_PB experts), then added in order q = 0, 1, ... The loads
+  // are unconditional, from clamped in-bounds addresses (MAXKS >= KS slots; extra slots repeat partial
+  // KS - 1 and are not added), so no load sits behind a branch whose join would wait for it.
+  constexpr int SEL_PB = 4;
+#pragma unroll
+  for (int p0 = 0; p0 < SEL_MAX_P; p0 += SEL_PB) {
+    if (p0 >= P) break;
+    if (part) {
+      float pv[SEL_PB][MAXKS];
+      const int64_t nn = live ? n : N - 1;
+#pragma unroll
+      for (int pp = 0; pp < SEL_PB; ++pp) {
+        const int e = min(lane + 64 * (p0 + pp), E - 1);
+#pragma unroll
+        for (int q = 0; q < MAXKS; ++q) pv[pp][q] = part[(int64_t)min(q, KS - 1) * N * E + nn * E + e];
+      }
+#pragma unroll
+      for (int pp = 0; pp < SEL_PB; ++pp) {
+        float r = pv[pp][0];
+#pragma unroll
+        for (int q = 1; q < MAXKS; ++q)
+          if (q < KS) r = __fadd_rn(r, pv[pp][q]);
+        sraw[p0 + pp] = 1.0f / (1.0f + expf(-r));  // s = sigmoid(x W_g^T)
+      }
+    } else {
+#pragma unroll
+      for (int pp = 0; pp < SEL_PB; ++pp) {
+        const int e = lane + 64 * (p0 + pp);
+        sraw[p0 + pp] = p0 + pp < P && e < E && live ? scores[n * E + e] : 0.f;
+      }
+    }
+  }
 #pragma unroll
   for (int p = 0; p < SEL_MAX_P; ++p) {
     const int e = lane + 64 * p;
     float sv = 0.f, bv = 0.f;
     if (p < P && e < E && live) {
-      if (part) {
-        // all KS partials are loaded before the first add, then added in order
-        float pv[SEL_MAX_KS];
-#pragma unroll
-        for (int q = 0; q < SEL_MAX_KS; ++q) pv[q] = q < KS ? part[(int64_t)q * N * E + n * E + e] : 0.f;
-        float r = pv[0];
-#pragma unroll
-        for (int q = 1; q < SEL_MAX_KS; ++q)
-          if (q < KS) r = __fadd_rn(r, pv[q]);
-        sv = 1.0f / (1.0f + expf(-r));  // s = sigmoid(x W_g^T)
-        scores[n * E + e] = sv;
-      } else {
-        sv = scores[n * E + e];
-      }
+      sv = sraw[p];
+      if (part) scores[n * E + e] = sv;
       bv = bias[e];
     }
     sp[p] = __fadd_rn(sv, bv);  // s' = s + b
@@ -392,8 +415,20 @@ hipError_t launch_logits(int dtype, const RouterPlan& p, const void* x, const fl
 hipError_t launch_select(float* scores, const float* part, int KS, const float* bias, int64_t N, int E, int G, int TG,
                          int k, float alpha, int norm, float eps, int32_t* idx, float* w, hipStream_t s) {
   dim3 grid((unsigned)((N + 3) / 4));
-  hipLaunchKernelGGL(select_kernel, grid, dim3(256), 0, s, scores, part, KS, bias, N, E, G, TG, k, alpha, norm, eps, idx,
-                     w);
+  // partial slots: the smallest power of two >= KS (KS <= SEL_MAX_KS); 1 when the scores are read
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(256), 0, s, scores, part, KS, bias, N, E, G, TG, k, alpha, norm, eps, idx, w);
+  };
+  if (!part || KS <= 1)
+    go(select_kernel<1>);
+  else if (KS <= 2)
+    go(select_kernel<2>);
+  else if (KS <= 4)
+    go(select_kernel<4>);
+  else if (KS <= 8)
+    go(select_kernel<8>);
+  else
+    go(select_kernel<SEL_MAX_KS>);
   return hipGetLastError();
 }
 
