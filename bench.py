@@ -161,8 +161,8 @@ def algorithmic_bytes(w: synth.Workload, N: int, distinct: int) -> dict:
 
 
 def is_decode(w: synth.Workload) -> bool:
-    """Token-poor batches (under 12 rows per expert on average) run the weight-streaming kernels."""
-    return w.N * w.k < 12 * w.E
+    """Batches under 28 rows per expert on average run the weight-streaming kernels."""
+    return w.N * w.k < 28 * w.E
 
 
 def measure(w: synth.Workload, r: dict) -> dict:

@@ -141,6 +141,9 @@ int64_t max_tiles(int64_t N, int k, int E, int n_shared_problem, int bm) {
 #ifndef MOE_DECODE_ROWS
 #define MOE_DECODE_ROWS 12  // average rows per expert below which the decode kernels run
 #endif
+#ifndef MOE_MID_ROWS
+#define MOE_MID_ROWS 28  // below this average rows per expert the decode kernels run with 64-row tiles
+#endif
 #ifndef MOE_BM256_ROWS
 #define MOE_BM256_ROWS 64  // average rows per expert from which the prefill GEMMs use 256-row tiles
 #endif
@@ -148,18 +151,19 @@ int64_t max_tiles(int64_t N, int k, int E, int n_shared_problem, int bm) {
 int gemm_bm(int dtype, int64_t N, int k, int E) {
   if (dtype == MOE_F32) return F_BM;
   if (N * k < (int64_t)MOE_DECODE_ROWS * E) return 16;  // weight-streaming decode kernel, 16-row tiles
+  if (N * k < (int64_t)MOE_MID_ROWS * E) return 64;     // the same kernel, 64-row tiles
   return N * k >= (int64_t)MOE_BM256_ROWS * E ? 256 : 128;  // 256-row tiles for row-heavy experts
 }
 
 hipError_t launch_gate_up(int dtype, const GroupedArgs& a, int64_t max_tile_count, hipStream_t s) {
   if (dtype == MOE_F32) return launch_grouped(grouped_f32<true>, a, max_tile_count, F_BN / 2, s);
-  if (a.bm == 16) return launch_bf16_decode(true, a, max_tile_count, s);
+  if (a.bm <= 64) return launch_bf16_decode(true, a, max_tile_count, s);
   return launch_bf16_prefill(true, a.bm, a, max_tile_count, s);
 }
 
 hipError_t launch_down(int dtype, const GroupedArgs& a, int64_t max_tile_count, hipStream_t s) {
   if (dtype == MOE_F32) return launch_grouped(grouped_f32<false>, a, max_tile_count, F_BN, s);
-  if (a.bm == 16) return launch_bf16_decode(false, a, max_tile_count, s);
+  if (a.bm <= 64) return launch_bf16_decode(false, a, max_tile_count, s);
   return launch_bf16_prefill(false, a.bm, a, max_tile_count, s);
 }
 
