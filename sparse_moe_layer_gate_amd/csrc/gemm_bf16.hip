@@ -353,12 +353,329 @@ __global__ __launch_bounds__(256, 1) void grouped_bf16_lds(GroupedArgs a, int nc
   }
 }
 
+// ---- eight-wave ping-pong kernel for 256-row tiles ----
+//
+// With one wave per SIMD, the wave that issues a K step's direct loads stalls while the texture path
+// accepts them (measured: a CU takes its 1 KiB global_load_lds_dwordx4 instructions at ~26-30 bytes
+// per clock, so the 64 KiB of operands of a 256 x 256 x 64 step hold a wave about as long as the
+// step's MFMAs run), and its SIMD's matrix core idles meanwhile. Here each SIMD runs two waves, one
+// from each half of the block (waves w and w + 4 share a SIMD), and the halves take turns: one issues
+// MFMAs while the other reads its next operand fragments from LDS and issues a quarter of a step's
+// direct loads, so the load path's back-pressure falls on the wave that is not feeding the matrix core.
+//  - block tile 256 x 256, BK = 64 (whole 128-byte lines per row and load); A in a two-stage ring, B
+//    in a three-stage ring, together all 160 KiB of LDS; rows chunk-swizzled as in PrefillTile;
+//  - half g (waves 4-7: g = 0, waves 0-3: g = 1) owns tile rows [128 g, 128 g + 128); wave w % 4 =
+//    2 wn + mh owns 64 rows (mh) of that half and 128 B rows (wn), as 2 x 4 tiles of
+//    v_mfma_f32_32x32x16_bf16 (gate_up: 64 gate rows and the matching 64 up rows, so SwiGLU pairs stay
+//    in one wave);
+//  - half g loads rows [128 g, 128 g + 128) of both operands (four direct loads per lane and quarter);
+//  - a K step is four barrier-separated slots, each covering half of the step's K range (lo / hi) for
+//    one half of the block, with the other half reading fragments and loading:
+//      slot 4t:     half 0 computes (t, lo)  half 1 reads (t, lo), loads its A rows of step t + 1
+//      slot 4t + 1: half 1 computes (t, lo)  half 0 reads (t, hi), loads its B rows of step t + 2
+//      slot 4t + 2: half 0 computes (t, hi)  half 1 reads (t, hi), loads its B rows of step t + 2;
+//                   both wait for step t + 1
+//      slot 4t + 3: half 1 computes (t, hi)  half 0 reads (t + 1, lo), loads its A rows of step t + 2
+//    Each slot carries 16 KiB of loads. A stage is refilled only after its last reader (half 1, slot
+//    4t + 2) has passed a barrier; A loads get two or three slots to land, B loads four or five.
+template <bool GATE_UP>
+struct PingPongTile {
+  static constexpr int BM = 256, BN = 256, BK = 64;
+  static constexpr int ROWB = BK * 2;          // bytes per LDS row
+  static constexpr int OPB = 256 * ROWB;       // one operand's bytes per stage (32 KiB)
+  static constexpr int A_STAGES = 2, B_STAGES = 3;
+  static constexpr int B_BASE = A_STAGES * OPB;
+  static constexpr int RING = (A_STAGES + B_STAGES) * OPB;
+  static constexpr int NL = 4;                 // direct loads per lane and quarter (128 rows of one operand)
+  static constexpr int COLS = GATE_UP ? BN / 2 : BN;  // output columns per block
+  static constexpr int OC = GATE_UP ? 64 : 128;       // output columns per wave
+  __device__ static int swz(int r) {
+    r &= 31;
+    return (r ^ (r >> 3)) & 7;
+  }
+  // LDS row (within a B stage) of the wave's column tile j
+  __device__ static int b_row(int j, int wn) {
+    if (GATE_UP) return (j < 2 ? 0 : BN / 2) + wn * 64 + (j & 1) * 32;
+    return wn * 128 + j * 32;
+  }
+};
+
+// Word 3 of a raw (untyped, stride 0) buffer descriptor on gfx9-family parts: 32-bit data format, no
+// swizzle, no index stride.
+constexpr int kRawBufferWord3 = 0x00020000;
+constexpr uint32_t kNoRow = 0xffffffffu;  // marks a direct-load lane that loads nothing
+
+// s_waitcnt lgkmcnt(0), other counters at their maximum
+__device__ inline void wait_lgkm0() { __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8)); }
+// Workgroup barrier without the memory-counter waits __syncthreads() adds (callers wait for exactly
+// what they need first); the signal fences keep the compiler from moving memory accesses across it.
+__device__ inline void bare_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// The K loop of one wave. offA / offB: byte offsets of this wave's direct-load sources in its half's
+// rows (A lanes of rows past the tile's valid rows load nothing; B is never skipped, so a wave's newest
+// NL loads are always B loads, which is what the vmcnt(NL) waits rely on).
+template <bool GATE_UP, int MI>
+__device__ __attribute__((always_inline)) inline void pingpong_loop(char* lds, __amdgpu_buffer_rsrc_t rsrcA,
+                                                                    const uint32_t (&offA)[4],
+                                                                    __amdgpu_buffer_rsrc_t rsrcB,
+                                                                    const uint32_t (&offB)[4], f32x16 (&acc)[2][4],
+                                                                    int nk, int grp, int q, int lane, int m0, int wn) {
+  using T = PingPongTile<GATE_UP>;
+  constexpr int NL = T::NL, TN = 4, ROWB = T::ROWB;
+  const int sw = T::swz(lane & 31);
+  const int a_off = (m0 + (lane & 31)) * ROWB;
+  int b_off[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) b_off[j] = (T::b_row(j, wn) + (lane & 31)) * ROWB;
+  // fragments of the lo and hi K halves in separate registers
+  bf16x8 af[2][2][MI > 0 ? MI : 1], bfr[2][2][TN];
+  const int half_off = grp * (T::OPB / 2) + q * 1024;  // this wave's first LDS chunk run in a stage
+
+  // this wave's loads of step kstep: load i fills chunks [(4 i + q) 64, + 64) of its half's rows; the K
+  // offset rides in the scalar offset
+  auto issue_a = [&](int kstep) {
+    char* dst = lds + (kstep % T::A_STAGES) * T::OPB + half_off;
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+      if (offA[i] != kNoRow)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrcA, (lds_void*)(dst + i * 4096), 16, (int)offA[i], kstep * T::BK * 2,
+                                                 0, 0);
+  };
+  auto issue_b = [&](int kstep) {
+    char* dst = lds + T::B_BASE + (kstep % T::B_STAGES) * T::OPB + half_off;
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrcB, (lds_void*)(dst + i * 4096), 16, (int)offB[i], kstep * T::BK * 2,
+                                               0, 0);
+  };
+  // operand fragments of K slices 2h, 2h + 1 of step kstep; waits for them
+  auto read_frags = [&](int kstep, int h) {
+    const char* sa = lds + (kstep % T::A_STAGES) * T::OPB;
+    const char* sb = lds + T::B_BASE + (kstep % T::B_STAGES) * T::OPB;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int coff = ((2 * (2 * h + s) + (lane >> 5)) ^ sw) * 16;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bfr[h][s][j] = *(const bf16x8*)(sb + b_off[j] + coff);
+#pragma unroll
+      for (int i = 0; i < MI; ++i) af[h][s][i] = *(const bf16x8*)(sa + a_off + i * 32 * ROWB + coff);
+    }
+    wait_lgkm0();
+  };
+  auto compute = [&](int h) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[h][s][i], bfr[h][s][j], acc[i][j], 0, 0, 0);
+  };
+
+  // prologue: this half's rows of A(0), B(0), B(1); wait for step 0
+  issue_a(0);
+  issue_b(0);
+  if (nk > 1) {
+    issue_b(1);
+    wait_vmcnt<NL>();
+  } else {
+    wait_vmcnt<0>();
+  }
+  bare_barrier();
+  // The two halves run separate straight-line loops (a wave's role never changes); both execute the
+  // same sequence of barriers, 4 per K step.
+  if (grp == 0) {
+    read_frags(0, 0);
+    if (nk > 1) issue_a(1);
+    bare_barrier();
+    for (int kt = 0; kt < nk; ++kt) {
+      compute(0);  // (kt, lo)
+      bare_barrier();
+      read_frags(kt, 1);
+      if (kt + 2 < nk) issue_b(kt + 2);
+      bare_barrier();
+      compute(1);  // (kt, hi)
+      // step kt + 1 has landed (only this wave's B loads of step kt + 2 may still be in flight)
+      if (kt + 2 < nk)
+        wait_vmcnt<NL>();
+      else
+        wait_vmcnt<0>();
+      bare_barrier();
+      if (kt + 1 < nk) {
+        read_frags(kt + 1, 0);
+        if (kt + 2 < nk) issue_a(kt + 2);
+      }
+      bare_barrier();
+    }
+  } else {
+    bare_barrier();
+    for (int kt = 0; kt < nk; ++kt) {
+      read_frags(kt, 0);
+      if (kt + 1 < nk) issue_a(kt + 1);
+      bare_barrier();
+      compute(0);  // (kt, lo)
+      bare_barrier();
+      read_frags(kt, 1);
+      if (kt + 2 < nk) issue_b(kt + 2);
+      if (kt + 2 < nk)
+        wait_vmcnt<NL>();
+      else
+        wait_vmcnt<0>();
+      bare_barrier();
+      compute(1);  // (kt, hi)
+      bare_barrier();
+    }
+  }
+}
+
+template <bool GATE_UP>
+__global__ __launch_bounds__(512, 1) void grouped_bf16_pp(GroupedArgs a, int ncol_max) {
+  using T = PingPongTile<GATE_UP>;
+  constexpr int NL = T::NL, OC = T::OC;
+  constexpr int OPITCH = OC + 8;  // bf16 per staged output row (16-byte pad)
+  constexpr int OUT_BYTES = 8 * 64 * OPITCH * 2;
+  constexpr int WROW_OFF = OUT_BYTES;  // row scales (down), after the staged outputs
+  static_assert(T::RING <= 160 * 1024 && WROW_OFF + 256 * 4 <= T::RING, "LDS budget");
+  __shared__ __attribute__((aligned(1024))) char lds[T::RING];
+
+  const int64_t n_tiles = *a.n_tiles;
+  const int64_t L = xcd_logical_block(n_tiles * ncol_max);
+  if (L < 0) return;
+  constexpr int GR = GATE_UP ? MOE_PF_GROUP_ROWS_GU : MOE_PF_GROUP_ROWS_DN;
+  const int64_t sg = L / ((int64_t)GR * ncol_max), within = L % ((int64_t)GR * ncol_max);
+  const int64_t gr = min((int64_t)GR, n_tiles - sg * GR);
+  const int64_t tile_id = sg * GR + within % gr;
+  const int ct = (int)(within / gr);
+  const Tile tile = a.tiles[tile_id];
+  const ExpertProblem P = pick_problem(a, tile.problem);
+  const int col0 = ct * T::COLS;
+  if (col0 >= P.ncols) return;
+
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  // Waves 4-7 form half 0 (which computes first) and waves 0-3 half 1. Measured: LDS reads issued in
+  // a slot where the other wave of the SIMD still has MFMAs waiting for the matrix core come back
+  // slower for the younger wave of the pair, and half 1 reads in exactly those slots (4t, 4t + 2);
+  // handing them to the older waves cut the gate_up time by 4-5%.
+  const int grp = 1 - (wave >> 2), q = wave & 3;
+  const int m0 = grp * 128 + (q & 1) * 64, wn = q >> 1;
+
+  // Direct-load sources: chunk p of this half's 128 rows is row 128 g + p / 8, slot p % 8, which holds
+  // the row's logical chunk slot ^ swz(row). Both operands are read through raw buffer descriptors
+  // with 32-bit byte offsets: B over the expert's matrix (the rows of one half come from one matrix:
+  // gate_up's half 0 loads gate rows, half 1 up rows), A over the tile's rows, or over all of x when
+  // rows are gathered (the launcher checks that x spans less than 4 GiB). No range clamping: every
+  // offset is in bounds.
+  const uint16_t* bbase =
+      (const uint16_t*)(GATE_UP && grp == 1 ? P.B1 : P.B0) + (int64_t)tile.expert * P.b_stride;
+  const uint16_t* abase = (const uint16_t*)P.A + (P.gather ? 0 : (int64_t)tile.row_start * P.lda);
+  const __amdgpu_buffer_rsrc_t rsrcB = __builtin_amdgcn_make_buffer_rsrc((void*)bbase, (short)0, -1, kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t rsrcA = __builtin_amdgcn_make_buffer_rsrc((void*)abase, (short)0, -1, kRawBufferWord3);
+  uint32_t offA[4], offB[4];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int p = (i * 4 + q) * 64 + lane;
+    const int r = grp * 128 + (p >> 3), c = (p & 7) ^ T::swz(r);
+    const int col = min(col0 + (GATE_UP ? r % (T::BN / 2) : r), P.ncols - 1);
+    offB[i] = ((uint32_t)col * (uint32_t)P.K + 8 * c) * 2;
+    if (r < tile.rows) {
+      const int64_t g = P.gather ? a.sorted_pair[(int64_t)tile.row_start + r] / a.k : r;
+      offA[i] = (uint32_t)(g * P.lda + 8 * c) * 2;
+    } else {
+      offA[i] = kNoRow;  // past the tile's valid rows: not loaded
+    }
+  }
+  // down: this thread's row scale, read now so its latency hides under the K loop
+  float wscale = 1.0f;
+  if (!GATE_UP && t < 256 && P.scale_rows) wscale = a.topk_w[a.sorted_pair[tile.row_start + min(t, tile.rows - 1)]];
+
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nk = P.K / T::BK;
+  const int live_m = tile.rows - m0;
+  const int mi = live_m <= 0 ? 0 : min(2, (live_m + 31) / 32);
+  if (mi == 2)
+    pingpong_loop<GATE_UP, 2>(lds, rsrcA, offA, rsrcB, offB, acc, nk, grp, q, lane, m0, wn);
+  else if (mi == 1)
+    pingpong_loop<GATE_UP, 1>(lds, rsrcA, offA, rsrcB, offB, acc, nk, grp, q, lane, m0, wn);
+  else
+    pingpong_loop<GATE_UP, 0>(lds, rsrcA, offA, rsrcB, offB, acc, nk, grp, q, lane, m0, wn);
+
+  // Epilogue through LDS (the loop ended on a barrier after the last operand read): each wave stages
+  // its 64 x OC bf16 results (SwiGLU / weight scale applied) in its own padded region, then stores
+  // whole 16-byte row chunks.
+  float* wrow = (float*)(lds + WROW_OFF);
+  if (!GATE_UP) {
+    if (t < 256) wrow[t] = wscale;
+    __syncthreads();
+  }
+  uint16_t* stage_out = (uint16_t*)lds + wave * (64 * OPITCH);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    if (i >= mi) continue;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);  // within the wave's 64 rows
+      if (GATE_UP) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          stage_out[row * OPITCH + j * 32 + (lane & 31)] = bf16_rne(swiglu(acc[i][j][r], acc[i][j + 2][r], a.swiglu_limit));
+      } else {
+        const float sc = wrow[m0 + row];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) stage_out[row * OPITCH + j * 32 + (lane & 31)] = bf16_rne(acc[i][j][r] * sc);
+      }
+    }
+  }
+  __syncthreads();
+  uint16_t* out = (uint16_t*)P.out;
+  const int ocol0 = col0 + wn * OC;
+  constexpr int CH = OC / 8;  // 16-byte chunks per staged row
+  const int rows_here = min(64, tile.rows - m0);
+  for (int c = lane; c < rows_here * CH; c += 64) {
+    const int row = c / CH, ch = c % CH;
+    const int col = ocol0 + ch * 8;
+    if (col < P.ncols) {  // ncols is a multiple of 64: a chunk is wholly in or out
+      const uint4 v = *(const uint4*)(stage_out + row * OPITCH + ch * 8);
+      *(uint4*)(out + ((int64_t)tile.row_start + m0 + row) * P.ldo + col) = v;
+    }
+  }
+}
+
+#ifndef MOE_PF_PINGPONG
+#define MOE_PF_PINGPONG 1
+#endif
+
 #ifndef MOE_PF_BK
 #define MOE_PF_BK 64
 #endif
 #ifndef MOE_PF_STAGES
 #define MOE_PF_STAGES 2
 #endif
+
+// The ping-pong kernel addresses its operands with 32-bit byte offsets: from x for gathered rows,
+// from a tile's first row otherwise, and from an expert's matrix for B.
+bool pingpong_fits(const GroupedArgs& a) {
+  constexpr int64_t LIM = int64_t(1) << 32;
+  for (int p = 0; p < 2; ++p) {
+    const ExpertProblem& P = a.prob[p];
+    if (!P.out) continue;
+    const int64_t a_rows = P.gather ? a.gather_rows : 256;
+    if (a_rows <= 0 || a_rows * P.lda * 2 >= LIM) return false;
+    if ((int64_t)P.ncols * P.K * 2 >= LIM) return false;
+  }
+  return true;
+}
 
 template <bool GATE_UP>
 hipError_t launch_bm(int bm, const GroupedArgs& a, int64_t max_tile_count, hipStream_t s) {
@@ -368,7 +685,9 @@ hipError_t launch_bm(int bm, const GroupedArgs& a, int64_t max_tile_count, hipSt
     if (a.prob[p].out) nc = max(nc, (a.prob[p].ncols + COLS - 1) / COLS);
   int64_t blocks = (max_tile_count * nc + 7) / 8 * 8;
   if (blocks == 0) return hipSuccess;
-  if (bm == 256)
+  if (bm == 256 && MOE_PF_PINGPONG && pingpong_fits(a))
+    hipLaunchKernelGGL((grouped_bf16_pp<GATE_UP>), dim3((unsigned)blocks), dim3(512), 0, s, a, nc);
+  else if (bm == 256)
     hipLaunchKernelGGL((grouped_bf16_lds<256, MOE_PF_BK, MOE_PF_STAGES, GATE_UP>), dim3((unsigned)blocks), dim3(256),
                        0, s, a, nc);
   else

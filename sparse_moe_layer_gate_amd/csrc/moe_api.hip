@@ -215,6 +215,7 @@ moe_status experts_impl(const moe_config* cfg, int64_t N, const void* x, const m
   g.k = k;
   g.offsets = at<int32_t>(ws, L.offsets);
   g.swiglu_limit = cfg->swiglu_limit;
+  g.gather_rows = N;
   // gate_up + SwiGLU: routed rows gather x through sorted_pair; the shared expert reads x in order
   g.tiles = at<Tile>(ws, L.tiles0);
   g.n_tiles = at<int32_t>(ws, L.ntiles);

@@ -117,6 +117,7 @@ struct GroupedArgs {
   int k;
   const int32_t* offsets;  // routed experts' row offsets [E + 1] (or nullptr: every expert counts as large)
   float swiglu_limit;      // gate_up epilogue clamp bound (0: plain SwiGLU)
+  int64_t gather_rows;     // rows of the matrix that gathered A rows index (x); 0 when unknown
 };
 // Field-wise select keeps a problem descriptor in scalar registers (a dynamically indexed
 // kernel-argument array would be copied to scratch).
