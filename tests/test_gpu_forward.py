@@ -36,6 +36,9 @@ SMALL = [
     dict(N=1000, D=512, E=8, G=1, TG=1, k=2, d=256, n_shared=1, alpha=1.0),
     # experts averaging 384+ rows: 256-row tiles, with column tails on both GEMMs
     dict(N=2000, D=320, E=8, G=2, TG=1, k=2, d=192, n_shared=1, alpha=2.5),
+    # 256-row tiles with one- and two-step K loops (D = 64 / 128, d = 128 / 64), skewed loads
+    dict(N=700, D=64, E=4, G=1, TG=1, k=2, d=128, n_shared=1, alpha=2.5, skew=1.0),
+    dict(N=900, D=128, E=6, G=2, TG=1, k=2, d=64, n_shared=0, alpha=2.5),
     dict(N=77, D=256, E=32, G=8, TG=3, k=6, d=128, n_shared=2, alpha=2.5),
     dict(N=129, D=192, E=12, G=1, TG=1, k=3, d=64, n_shared=0, alpha=2.5),
     dict(N=50, D=256, E=16, G=4, TG=2, k=4, d=128, n_shared=1, alpha=2.5, norm=False),
