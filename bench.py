@@ -67,11 +67,11 @@ def read_traffic(workload: str) -> dict | None:
         return None
 
 
-KERNEL_NAMES = {  # library stage -> substring of the HIP kernel symbol
-    "experts_gate_up": ("grouped_bf16_lds<", "true>"),
-    "experts_down": ("grouped_bf16_lds<", "false>"),
-    "experts_gate_up_decode": ("grouped_bf16_decode<true>", ""),
-    "experts_down_decode": ("grouped_bf16_decode<false>", ""),
+KERNEL_NAMES = {  # library stage -> substrings of the HIP kernel symbols that run it (first match wins)
+    "experts_gate_up": [("grouped_bf16_pp<true>", ""), ("grouped_bf16_lds<", "true>")],
+    "experts_down": [("grouped_bf16_pp<false>", ""), ("grouped_bf16_lds<", "false>")],
+    "experts_gate_up_decode": [("grouped_bf16_decode<true,", "")],
+    "experts_down_decode": [("grouped_bf16_decode<false,", "")],
 }
 
 
@@ -125,8 +125,8 @@ def profile_summary(pdir: str, workload: str, decode: bool) -> str:
     for k in fetch:
         if k in write:
             lines.append(f"| `{k[:90]}` | {fetch[k] * f_scale / 1e9:.3f} | {write[k] * w_scale / 1e9:.3f} |")
-    key = KERNEL_NAMES["experts_gate_up_decode" if decode else "experts_gate_up"]
-    dom = [k for k in fetch if key[0] in k and key[1] in k]
+    dom = [k for a, b in KERNEL_NAMES["experts_gate_up_decode" if decode else "experts_gate_up"]
+           for k in fetch if a in k and b in k]
     if dom:
         k = dom[0]
         fb, wb = fetch[k] * f_scale, write.get(k, 0.0) * w_scale
