@@ -685,13 +685,11 @@ hipError_t launch_bm(int bm, const GroupedArgs& a, int64_t max_tile_count, hipSt
     if (a.prob[p].out) nc = max(nc, (a.prob[p].ncols + COLS - 1) / COLS);
   int64_t blocks = (max_tile_count * nc + 7) / 8 * 8;
   if (blocks == 0) return hipSuccess;
-  if (bm == 256 && MOE_PF_PINGPONG && pingpong_fits(a))
+  if (bm != 256) return hipErrorInvalidValue;  // the forward builds 256-row tile lists for these kernels
+  if (MOE_PF_PINGPONG && pingpong_fits(a))
     hipLaunchKernelGGL((grouped_bf16_pp<GATE_UP>), dim3((unsigned)blocks), dim3(512), 0, s, a, nc);
-  else if (bm == 256)
-    hipLaunchKernelGGL((grouped_bf16_lds<256, MOE_PF_BK, MOE_PF_STAGES, GATE_UP>), dim3((unsigned)blocks), dim3(256),
-                       0, s, a, nc);
   else
-    hipLaunchKernelGGL((grouped_bf16_lds<128, MOE_PF_BK, MOE_PF_STAGES, GATE_UP>), dim3((unsigned)blocks), dim3(256),
+    hipLaunchKernelGGL((grouped_bf16_lds<256, MOE_PF_BK, MOE_PF_STAGES, GATE_UP>), dim3((unsigned)blocks), dim3(256),
                        0, s, a, nc);
   return hipGetLastError();
 }
