@@ -70,8 +70,8 @@ def read_traffic(workload: str) -> dict | None:
 KERNEL_NAMES = {  # library stage -> substrings of the HIP kernel symbols that run it (first match wins)
     "experts_gate_up": [("grouped_bf16_pp<true>", ""), ("grouped_bf16_lds<", "true>")],
     "experts_down": [("grouped_bf16_pp<false>", ""), ("grouped_bf16_lds<", "false>")],
-    "experts_gate_up_decode": [("grouped_bf16_decode<true,", "")],
-    "experts_down_decode": [("grouped_bf16_decode<false,", "")],
+    "experts_gate_up_decode": [("grouped_bf16_decode<true", "")],
+    "experts_down_decode": [("grouped_bf16_decode<false", "")],
 }
 
 
@@ -161,8 +161,8 @@ def algorithmic_bytes(w: synth.Workload, N: int, distinct: int) -> dict:
 
 
 def is_decode(w: synth.Workload) -> bool:
-    """Batches under 28 rows per expert on average run the weight-streaming kernels."""
-    return w.N * w.k < 28 * w.E
+    """Batches under 8 rows per expert on average run the weight-streaming kernels."""
+    return w.N * w.k < 8 * w.E
 
 
 def measure(w: synth.Workload, r: dict) -> dict:

@@ -139,29 +139,28 @@ int64_t max_tiles(int64_t N, int k, int E, int n_shared_problem, int bm) {
 }
 
 #ifndef MOE_DECODE_ROWS
-#define MOE_DECODE_ROWS 12  // average rows per expert below which the decode kernels run
-#endif
-#ifndef MOE_MID_ROWS
-#define MOE_MID_ROWS 28  // below this average rows per expert the decode kernels run with 64-row tiles
+#define MOE_DECODE_ROWS 8  // average rows per expert below which the decode kernels run
 #endif
 
 int gemm_bm(int dtype, int64_t N, int k, int E) {
   if (dtype == MOE_F32) return F_BM;
+  // Measured (prefill kernel = the ping-pong kernel): with uniform routing the two kernels tie at ~8
+  // rows per expert and the decode kernel is 4-15% ahead at 6-7; with skewed routing the decode
+  // kernel's 16-row tiles re-stream a hot expert's weights once per 16 rows and lose 28-37% already
+  // at 6-10 rows per expert on average.
   if (N * k < (int64_t)MOE_DECODE_ROWS * E) return 16;  // weight-streaming decode kernel, 16-row tiles
-  if (N * k < (int64_t)MOE_MID_ROWS * E) return 64;     // the same kernel, 64-row tiles
-  return 256;  // prefill kernels, 256-row tiles (measured: from 28 rows per expert on they beat the
-               // 64-row streaming tiles, and 128-row tiles of the four-wave kernel by 8-15% at 32-64)
+  return 256;                                           // prefill kernels, 256-row tiles
 }
 
 hipError_t launch_gate_up(int dtype, const GroupedArgs& a, int64_t max_tile_count, hipStream_t s) {
   if (dtype == MOE_F32) return launch_grouped(grouped_f32<true>, a, max_tile_count, F_BN / 2, s);
-  if (a.bm <= 64) return launch_bf16_decode(true, a, max_tile_count, s);
+  if (a.bm == 16) return launch_bf16_decode(true, a, max_tile_count, s);
   return launch_bf16_prefill(true, a.bm, a, max_tile_count, s);
 }
 
 hipError_t launch_down(int dtype, const GroupedArgs& a, int64_t max_tile_count, hipStream_t s) {
   if (dtype == MOE_F32) return launch_grouped(grouped_f32<false>, a, max_tile_count, F_BN, s);
-  if (a.bm <= 64) return launch_bf16_decode(false, a, max_tile_count, s);
+  if (a.bm == 16) return launch_bf16_decode(false, a, max_tile_count, s);
   return launch_bf16_prefill(false, a.bm, a, max_tile_count, s);
 }
 

@@ -3,8 +3,7 @@
 // With one or two tokens per expert the layer is a weight stream ("Module 02 -- MoE: Capacity, Work,
 // and Traffic", section 1: traffic, not arithmetic, governs decode), so this kernel is built to keep
 // many weight bytes in flight and to move each weight byte once, in whole cache lines:
-//  - row tiles of at most 16 rows (token-poor batches) or 64 rows (a few tens of rows per expert), the
-//    latter held as four 16-row sub-tiles that share every weight stage;
+//  - row tiles of at most 16 rows (the tile list is built with 16 rows per tile);
 //  - each wave owns NT 16-column tiles of one expert (gate_up: NT/2 gate and NT/2 up tiles, SwiGLU in
 //    registers; down: NT tiles, each row scaled by its weight) and works alone: no block barriers;
 //  - loaded straight into registers, the MFMA operand layout (v_mfma_f32_16x16x32_bf16: a lane holds
@@ -24,10 +23,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 #ifndef MOE_DC_U
-#define MOE_DC_U 4  // K slices per stage with one 16-row sub-tile per tile
-#endif
-#ifndef MOE_DC_U_MID
-#define MOE_DC_U_MID 2  // K slices per stage with up to four 16-row sub-tiles per tile
+#define MOE_DC_U 4
 #endif
 #ifndef MOE_DC_S
 #define MOE_DC_S 2
@@ -36,165 +32,35 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 #define MOE_DC_NT 2
 #endif
 
-// RSMAX: 16-row sub-tiles a tile may hold (1 for 16-row tiles, 4 for 64-row tiles). Every wave of a
-// block holds the tile's activation rows as RSMAX sub-tiles, so a weight stage read from HBM feeds
-// the MFMAs of every row of the tile: an expert with up to 16 RSMAX rows streams its weights once.
-template <bool GATE_UP, int RSMAX>
+template <bool GATE_UP>
 struct DecodeTile {
-  static constexpr int NT = MOE_DC_NT;                     // 16-column weight tiles per wave
-  static constexpr int U = RSMAX == 1 ? MOE_DC_U : MOE_DC_U_MID;  // 32-wide K slices per stage
-  static constexpr int S = MOE_DC_S;                       // ring depth (stages)
-  static constexpr int SK = 32 * U;                        // K elements per stage
-  static constexpr int CPR = SK / 8;                       // 16-byte chunks per row and stage
-  static constexpr int RPI = 64 / CPR;                     // rows per DMA instruction
-  static constexpr int QPT = 16 / RPI;                     // DMA instructions per 16-row tile and stage
+  static constexpr int NT = MOE_DC_NT;  // 16-column weight tiles per wave
+  static constexpr int U = MOE_DC_U;    // 32-wide K slices per stage
+  static constexpr int S = MOE_DC_S;    // ring depth (stages)
+  static constexpr int SK = 32 * U;     // K elements per stage
+  static constexpr int CPR = SK / 8;    // 16-byte chunks per row and stage
+  static constexpr int RPI = 64 / CPR;  // rows per DMA instruction
+  static constexpr int QPT = 16 / RPI;  // DMA instructions per 16-row tile and stage
   static constexpr int TILE_BYTES = 16 * SK * 2;
-  static constexpr int STAGE_BYTES = (RSMAX + NT) * TILE_BYTES;  // activation sub-tiles, then weights
+  static constexpr int STAGE_BYTES = (NT + 1) * TILE_BYTES;  // activation tile, then NT weight tiles
   static constexpr int WAVE_BYTES = S * STAGE_BYTES;
+  static constexpr int NDMA = (NT + 1) * QPT;  // DMA instructions per stage
   static constexpr int WAVE_COLS = GATE_UP ? NT / 2 * 16 : NT * 16;  // output columns per wave
   static constexpr int BLOCK_COLS = 4 * WAVE_COLS;
   static_assert(!GATE_UP || NT % 2 == 0, "gate_up pairs gate and up tiles");
   static_assert(CPR >= 8 && CPR <= 64 && 64 % CPR == 0, "a DMA instruction covers whole 128-byte lines");
-  static_assert((S - 1) * (RSMAX + NT) * QPT < 64, "vmcnt is 6 bits");
+  static_assert((S - 1) * NDMA < 64, "vmcnt is 6 bits");
   static_assert(4 * WAVE_BYTES <= 160 * 1024, "LDS per CU");
 
   // Chunk swizzle: chunk c of row r sits in slot c ^ sig(r). For each MFMA operand read (16 lanes of
   // one k group over rows 0..15) the 16 slots then fall in distinct 16-byte bank groups.
   __device__ static int sig(int r) { return CPR >= 16 ? r : r / (16 / CPR); }
-
-  // The K loop and epilogue of a tile whose rows fill RS of the RSMAX sub-tiles.
-  template <int RS>
-  __device__ static __attribute__((always_inline)) void run(const GroupedArgs& a, const Tile& tile,
-                                                            const ExpertProblem& P, int wcol0, char* ring,
-                                                            int lane) {
-    constexpr int NDMA = (RS + NT) * QPT;  // DMA instructions per stage
-    // DMA sources of this lane: in instruction q of a 16-row (sub-)tile it moves chunk chunk[q] of
-    // row q * RPI + lane / CPR into slot lane % CPR of that row. Every lane of every instruction is
-    // active: activation rows past tile.rows repeat the last valid row and weight rows past ncols
-    // repeat the last column (neither reaches a stored output), so each stage is exactly NDMA
-    // instructions.
-    const uint16_t* src_a[RS][QPT];
-    const uint16_t* src_w[NT][QPT];
-    int chunk[QPT];
-#pragma unroll
-    for (int q = 0; q < QPT; ++q) {
-      const int r = q * RPI + lane / CPR;
-      chunk[q] = (lane % CPR) ^ sig(r);
-#pragma unroll
-      for (int rs = 0; rs < RS; ++rs) {
-        int64_t g = (int64_t)tile.row_start + min(16 * rs + r, tile.rows - 1);
-        if (P.gather) g = a.sorted_pair[g] / a.k;
-        src_a[rs][q] = (const uint16_t*)P.A + g * P.lda;
-      }
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        const uint16_t* base;
-        int col;
-        if (GATE_UP) {
-          base = (const uint16_t*)(j < NT / 2 ? P.B0 : P.B1);
-          col = wcol0 + (j % (NT / 2)) * 16 + r;
-        } else {
-          base = (const uint16_t*)P.B0;
-          col = wcol0 + j * 16 + r;
-        }
-        col = min(col, P.ncols - 1);
-        src_w[j][q] = base + (int64_t)tile.expert * P.b_stride + (int64_t)col * P.K;
-      }
-    }
-
-    const int nst = (P.K + SK - 1) / SK;
-    const int ktail = P.K - (nst - 1) * SK;  // K elements of the last stage (a multiple of 32)
-
-    // Stage t -> ring slot t % S. In a short last stage, chunks past K load the last chunk in K instead
-    // (their slots are never read), keeping every address inside its row.
-    auto issue = [&](int t) {
-      char* st = ring + (t % S) * STAGE_BYTES;
-      const int kmax = t == nst - 1 ? ktail : SK;
-#pragma unroll
-      for (int q = 0; q < QPT; ++q) {
-        const int64_t ke = (int64_t)t * SK + 8 * min(chunk[q], kmax / 8 - 1);
-#pragma unroll
-        for (int rs = 0; rs < RS; ++rs)
-          __builtin_amdgcn_global_load_lds((const void*)(src_a[rs][q] + ke),
-                                           (lds_void*)(st + rs * TILE_BYTES + q * 1024), 16, 0, 0);
-#pragma unroll
-        for (int j = 0; j < NT; ++j)
-          __builtin_amdgcn_global_load_lds((const void*)(src_w[j][q] + ke),
-                                           (lds_void*)(st + (RSMAX + j) * TILE_BYTES + q * 1024), 16, 0, 0);
-      }
-    };
-
-    const int r16 = lane & 15, kq = lane >> 4;  // MFMA operand row and 8-element k group of this lane
-    f32x4 acc[RS][NT];
-#pragma unroll
-    for (int rs = 0; rs < RS; ++rs)
-#pragma unroll
-      for (int j = 0; j < NT; ++j) acc[rs][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-#pragma unroll
-    for (int t = 0; t < S - 1; ++t)
-      if (t < nst) issue(t);
-    for (int t = 0; t < nst; ++t) {
-      // The refill of slot (t - 1) % S follows the reads of stage t - 1, which have completed: their
-      // values fed that stage's MFMAs.
-      if (t + S - 1 < nst) {
-        issue(t + S - 1);
-        wait_vmcnt<(S - 1) * NDMA>();
-      } else {
-        wait_vmcnt<0>();
-      }
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      const char* st = ring + (t % S) * STAGE_BYTES;
-      const int kmax = t == nst - 1 ? ktail : SK;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (32 * u >= kmax) break;
-        const int off = r16 * CPR * 16 + 16 * ((4 * u + kq) ^ sig(r16));
-        bf16x8 av[RS];
-#pragma unroll
-        for (int rs = 0; rs < RS; ++rs) av[rs] = *(const bf16x8*)(st + rs * TILE_BYTES + off);
-#pragma unroll
-        for (int j = 0; j < NT; ++j) {
-          const bf16x8 bv = *(const bf16x8*)(st + (RSMAX + j) * TILE_BYTES + off);
-#pragma unroll
-          for (int rs = 0; rs < RS; ++rs)
-            acc[rs][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[rs], bv, acc[rs][j], 0, 0, 0);
-        }
-      }
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    }
-
-    // 16x16 C layout: lane holds column lane % 16, rows 4 (lane / 16) + i of its sub-tile.
-    uint16_t* out = (uint16_t*)P.out;
-#pragma unroll
-    for (int rs = 0; rs < RS; ++rs)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 16 * rs + 4 * kq + i;
-        if (row >= tile.rows) continue;
-        const int64_t orow = (int64_t)tile.row_start + row;
-        if (GATE_UP) {
-#pragma unroll
-          for (int j = 0; j < NT / 2; ++j) {
-            const int col = wcol0 + j * 16 + r16;
-            if (col < P.ncols)
-              out[orow * P.ldo + col] = bf16_rne(swiglu(acc[rs][j][i], acc[rs][j + NT / 2][i], a.swiglu_limit));
-          }
-        } else {
-          const float sc = P.scale_rows ? a.topk_w[a.sorted_pair[orow]] : 1.0f;
-#pragma unroll
-          for (int j = 0; j < NT; ++j) {
-            const int col = wcol0 + j * 16 + r16;
-            if (col < P.ncols) out[orow * P.ldo + col] = bf16_rne(acc[rs][j][i] * sc);
-          }
-        }
-      }
-  }
 };
 
-template <bool GATE_UP, int RSMAX>
+template <bool GATE_UP>
 __global__ __launch_bounds__(256) void grouped_bf16_decode(GroupedArgs a, int ncol_max) {
-  using T = DecodeTile<GATE_UP, RSMAX>;
+  using T = DecodeTile<GATE_UP>;
+  constexpr int NT = T::NT, U = T::U, S = T::S, SK = T::SK, CPR = T::CPR, RPI = T::RPI, QPT = T::QPT;
   __shared__ __attribute__((aligned(1024))) char lds[4 * T::WAVE_BYTES];
 
   const int64_t L = xcd_logical_block((int64_t)*a.n_tiles * ncol_max);
@@ -209,35 +75,128 @@ __global__ __launch_bounds__(256) void grouped_bf16_decode(GroupedArgs a, int nc
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wcol0 = col0 + wave * T::WAVE_COLS;
   char* const ring = lds + wave * T::WAVE_BYTES;
-  const int rs = (tile.rows + 15) / 16;  // 1 .. RSMAX
-  if (RSMAX == 1 || rs <= 1)
-    T::template run<1>(a, tile, P, wcol0, ring, lane);
-  else if (rs == 2)
-    T::template run<RSMAX >= 2 ? 2 : 1>(a, tile, P, wcol0, ring, lane);
-  else if (rs == 3)
-    T::template run<RSMAX >= 3 ? 3 : 1>(a, tile, P, wcol0, ring, lane);
-  else
-    T::template run<RSMAX>(a, tile, P, wcol0, ring, lane);
+
+  // DMA sources of this lane: in instruction q of a tile it moves chunk chunk[q] of tile row
+  // q * RPI + lane / CPR into slot lane % CPR of that row. Every lane of every instruction is active:
+  // activation rows past tile.rows repeat the last valid row and weight rows past ncols repeat the
+  // last column (neither reaches a stored output), so each stage is exactly NDMA instructions.
+  const uint16_t* src[NT + 1][QPT];
+  int chunk[QPT];
+#pragma unroll
+  for (int q = 0; q < QPT; ++q) {
+    const int r = q * RPI + lane / CPR;
+    chunk[q] = (lane % CPR) ^ T::sig(r);
+    int64_t g = (int64_t)tile.row_start + min(r, tile.rows - 1);
+    if (P.gather) g = a.sorted_pair[g] / a.k;
+    src[0][q] = (const uint16_t*)P.A + g * P.lda;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const uint16_t* base;
+      int col;
+      if (GATE_UP) {
+        base = (const uint16_t*)(j < NT / 2 ? P.B0 : P.B1);
+        col = wcol0 + (j % (NT / 2)) * 16 + r;
+      } else {
+        base = (const uint16_t*)P.B0;
+        col = wcol0 + j * 16 + r;
+      }
+      col = min(col, P.ncols - 1);
+      src[1 + j][q] = base + (int64_t)tile.expert * P.b_stride + (int64_t)col * P.K;
+    }
+  }
+
+  const int nst = (P.K + SK - 1) / SK;
+  const int ktail = P.K - (nst - 1) * SK;  // K elements of the last stage (a multiple of 32)
+
+  // Stage t -> ring slot t % S. In a short last stage, chunks past K load the last chunk in K instead
+  // (their slots are never read), keeping every address inside its row.
+  auto issue = [&](int t) {
+    char* st = ring + (t % S) * T::STAGE_BYTES;
+    const int kmax = t == nst - 1 ? ktail : SK;
+#pragma unroll
+    for (int q = 0; q < QPT; ++q) {
+      const int64_t ke = (int64_t)t * SK + 8 * min(chunk[q], kmax / 8 - 1);
+#pragma unroll
+      for (int j = 0; j <= NT; ++j)
+        __builtin_amdgcn_global_load_lds((const void*)(src[j][q] + ke), (lds_void*)(st + j * T::TILE_BYTES + q * 1024),
+                                         16, 0, 0);
+    }
+  };
+
+  const int r16 = lane & 15, kq = lane >> 4;  // MFMA operand row and 8-element k group of this lane
+  f32x4 acc[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int t = 0; t < S - 1; ++t)
+    if (t < nst) issue(t);
+  for (int t = 0; t < nst; ++t) {
+    // The refill of slot (t - 1) % S follows the reads of stage t - 1, which have completed: their
+    // values fed that stage's MFMAs.
+    if (t + S - 1 < nst) {
+      issue(t + S - 1);
+      wait_vmcnt<(S - 1) * T::NDMA>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    const char* st = ring + (t % S) * T::STAGE_BYTES;
+    const int kmax = t == nst - 1 ? ktail : SK;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (32 * u >= kmax) break;
+      const int off = r16 * CPR * 16 + 16 * ((4 * u + kq) ^ T::sig(r16));
+      const bf16x8 av = *(const bf16x8*)(st + off);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const bf16x8 bv = *(const bf16x8*)(st + (1 + j) * T::TILE_BYTES + off);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[j], 0, 0, 0);
+      }
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  }
+
+  // 16x16 C layout: lane holds column lane % 16, rows 4 (lane / 16) + i.
+  uint16_t* out = (uint16_t*)P.out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 4 * kq + i;
+    if (row >= tile.rows) continue;
+    const int64_t orow = (int64_t)tile.row_start + row;
+    if (GATE_UP) {
+#pragma unroll
+      for (int j = 0; j < NT / 2; ++j) {
+        const int col = wcol0 + j * 16 + r16;
+        if (col < P.ncols) out[orow * P.ldo + col] = bf16_rne(swiglu(acc[j][i], acc[j + NT / 2][i], a.swiglu_limit));
+      }
+    } else {
+      const float sc = P.scale_rows ? a.topk_w[a.sorted_pair[orow]] : 1.0f;
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const int col = wcol0 + j * 16 + r16;
+        if (col < P.ncols) out[orow * P.ldo + col] = bf16_rne(acc[j][i] * sc);
+      }
+    }
+  }
 }
 
-template <bool GATE_UP, int RSMAX>
+template <bool GATE_UP>
 hipError_t launch(const GroupedArgs& a, int64_t max_tile_count, hipStream_t s) {
-  constexpr int BLOCK_COLS = DecodeTile<GATE_UP, RSMAX>::BLOCK_COLS;
+  constexpr int BLOCK_COLS = DecodeTile<GATE_UP>::BLOCK_COLS;
   int nc = 0;
   for (int p = 0; p < 2; ++p)
     if (a.prob[p].out) nc = max(nc, (a.prob[p].ncols + BLOCK_COLS - 1) / BLOCK_COLS);
   const int64_t blocks = (max_tile_count * nc + 7) / 8 * 8;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((grouped_bf16_decode<GATE_UP, RSMAX>), dim3((unsigned)blocks), dim3(256), 0, s, a, nc);
+  hipLaunchKernelGGL(grouped_bf16_decode<GATE_UP>, dim3((unsigned)blocks), dim3(256), 0, s, a, nc);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_bf16_decode(bool gate_up, const GroupedArgs& a, int64_t max_tile_count, hipStream_t s) {
-  if (a.bm == 16) return gate_up ? launch<true, 1>(a, max_tile_count, s) : launch<false, 1>(a, max_tile_count, s);
-  if (a.bm == 64) return gate_up ? launch<true, 4>(a, max_tile_count, s) : launch<false, 4>(a, max_tile_count, s);
-  return hipErrorInvalidValue;
+  return gate_up ? launch<true>(a, max_tile_count, s) : launch<false>(a, max_tile_count, s);
 }
 
 }  // namespace moe

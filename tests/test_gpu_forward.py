@@ -42,11 +42,12 @@ SMALL = [
     dict(N=77, D=256, E=32, G=8, TG=3, k=6, d=128, n_shared=2, alpha=2.5),
     dict(N=129, D=192, E=12, G=1, TG=1, k=3, d=64, n_shared=0, alpha=2.5),
     dict(N=50, D=256, E=16, G=4, TG=2, k=4, d=128, n_shared=1, alpha=2.5, norm=False),
-    # 64-row streaming tiles (12-28 rows per expert on average); the skewed router gives some experts
-    # several 64-row tiles and ragged sub-tile counts, with column tails and a short last K stage
+    # 256-row tiles holding few rows (~19 per expert), skewed: some experts span two tiles
     dict(N=150, D=320, E=16, G=1, TG=1, k=2, d=192, n_shared=1, alpha=2.5, skew=1.0),
-    # 16-row (decode) tiles with column tails and a short last K stage (D = 320, d = 192)
-    dict(N=40, D=320, E=24, G=4, TG=2, k=4, d=192, n_shared=1, alpha=2.5),
+    # 16-row (decode) tiles with column tails and a short last K stage (D = 320, d = 192); the
+    # skewed router gives some experts several 16-row tiles
+    dict(N=30, D=320, E=24, G=4, TG=2, k=4, d=192, n_shared=1, alpha=2.5),
+    dict(N=60, D=320, E=64, G=1, TG=1, k=4, d=192, n_shared=1, alpha=2.5, skew=1.0),
     dict(N=1, D=256, E=16, G=4, TG=2, k=4, d=128, n_shared=1, alpha=2.5),
     dict(N=3, D=128, E=8, G=2, TG=1, k=1, d=64, n_shared=1, alpha=2.5),
 ]
