@@ -353,33 +353,28 @@ __global__ __launch_bounds__(256, 1) void grouped_bf16_lds(GroupedArgs a, int nc
   }
 }
 
-// ---- eight-wave ping-pong kernel for 256-row tiles ----
+// ---- eight-wave kernel for 256-row tiles ----
 //
 // With one wave per SIMD, the wave that issues a K step's direct loads stalls while the texture path
-// accepts them (measured: a CU takes its 1 KiB global_load_lds_dwordx4 instructions at ~26-30 bytes
-// per clock, so the 64 KiB of operands of a 256 x 256 x 64 step hold a wave about as long as the
-// step's MFMAs run), and its SIMD's matrix core idles meanwhile. Here each SIMD runs two waves, one
-// from each half of the block (waves w and w + 4 share a SIMD), and the halves take turns: one issues
-// MFMAs while the other reads its next operand fragments from LDS and issues a quarter of a step's
-// direct loads, so the load path's back-pressure falls on the wave that is not feeding the matrix core.
+// accepts them (measured: a CU takes 1 KiB global_load_lds_dwordx4 instructions at ~26-30 bytes per
+// clock, so the 64 KiB of operands of a 256 x 256 x 64 step hold a wave about as long as the step's
+// MFMAs run), and its SIMD's matrix core idles meanwhile. Here each SIMD runs two waves (w and w + 4),
+// each with its own 64 x 128 share of the tile, its own fragment reads and an eighth of every step's
+// loads: while one of them waits on the load path, the other keeps the matrix core busy.
 //  - block tile 256 x 256, BK = 64 (whole 128-byte lines per row and load); A in a two-stage ring, B
 //    in a three-stage ring, together all 160 KiB of LDS; rows chunk-swizzled as in PrefillTile;
-//  - half g (waves 4-7: g = 0, waves 0-3: g = 1) owns tile rows [128 g, 128 g + 128); wave w % 4 =
-//    2 wn + mh owns 64 rows (mh) of that half and 128 B rows (wn), as 2 x 4 tiles of
-//    v_mfma_f32_32x32x16_bf16 (gate_up: 64 gate rows and the matching 64 up rows, so SwiGLU pairs stay
-//    in one wave);
-//  - half g loads rows [128 g, 128 g + 128) of both operands (four direct loads per lane and quarter);
-//  - a K step is four barrier-separated slots, each covering half of the step's K range (lo / hi) for
-//    one half of the block, with the other half reading fragments and loading:
-//      slot 4t:     half 0 computes (t, lo)  half 1 reads (t, lo), loads its A rows of step t + 1
-//      slot 4t + 1: half 1 computes (t, lo)  half 0 reads (t, hi), loads its B rows of step t + 2
-//      slot 4t + 2: half 0 computes (t, hi)  half 1 reads (t, hi), loads its B rows of step t + 2;
-//                   both wait for step t + 1
-//      slot 4t + 3: half 1 computes (t, hi)  half 0 reads (t + 1, lo), loads its A rows of step t + 2
-//    Each slot carries 16 KiB of loads. A stage is refilled only after its last reader (half 1, slot
-//    4t + 2) has passed a barrier; A loads get two or three slots to land, B loads four or five.
+//  - half g = w / 4 owns tile rows [128 g, 128 g + 128); wave w % 4 = 2 wn + mh owns 64 rows (mh) of
+//    that half and 128 B rows (wn), as 2 x 4 tiles of v_mfma_f32_32x32x16_bf16 (gate_up: 64 gate rows
+//    and the matching 64 up rows, so SwiGLU pairs stay in one wave);
+//  - the waves of half g load rows [128 g, 128 g + 128) of both operands, four direct loads per lane
+//    of each per step (buffer_load_dwordx4 ... lds through raw buffer descriptors);
+//  - per K step t a wave reads the fragments of the step's first 32 K values, issues its A loads of
+//    step t + 1, reads the second half's fragments while the first half's MFMAs run, issues its B
+//    loads of step t + 2, runs the second half's MFMAs, waits for its loads of step t + 1 and meets
+//    the others at a barrier. A stage is refilled only after every wave has passed the barrier that
+//    follows its last read; A loads get about one step to land and B loads two.
 template <bool GATE_UP>
-struct PingPongTile {
+struct Wave8Tile {
   static constexpr int BM = 256, BN = 256, BK = 64;
   static constexpr int ROWB = BK * 2;          // bytes per LDS row
   static constexpr int OPB = 256 * ROWB;       // one operand's bytes per stage (32 KiB)
@@ -419,12 +414,11 @@ __device__ inline void bare_barrier() {
 // rows (A lanes of rows past the tile's valid rows load nothing; B is never skipped, so a wave's newest
 // NL loads are always B loads, which is what the vmcnt(NL) waits rely on).
 template <bool GATE_UP, int MI>
-__device__ __attribute__((always_inline)) inline void pingpong_loop(char* lds, __amdgpu_buffer_rsrc_t rsrcA,
-                                                                    const uint32_t (&offA)[4],
-                                                                    __amdgpu_buffer_rsrc_t rsrcB,
-                                                                    const uint32_t (&offB)[4], f32x16 (&acc)[2][4],
-                                                                    int nk, int grp, int q, int lane, int m0, int wn) {
-  using T = PingPongTile<GATE_UP>;
+__device__ __attribute__((always_inline)) inline void wave8_loop(char* lds, __amdgpu_buffer_rsrc_t rsrcA,
+                                                                 const uint32_t (&offA)[4], __amdgpu_buffer_rsrc_t rsrcB,
+                                                                 const uint32_t (&offB)[4], f32x16 (&acc)[2][4], int nk,
+                                                                 int grp, int q, int lane, int m0, int wn) {
+  using T = Wave8Tile<GATE_UP>;
   constexpr int NL = T::NL, TN = 4, ROWB = T::ROWB;
   const int sw = T::swz(lane & 31);
   const int a_off = (m0 + (lane & 31)) * ROWB;
@@ -452,7 +446,7 @@ __device__ __attribute__((always_inline)) inline void pingpong_loop(char* lds, _
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrcB, (lds_void*)(dst + i * 4096), 16, (int)offB[i], kstep * T::BK * 2,
                                                0, 0);
   };
-  // operand fragments of K slices 2h, 2h + 1 of step kstep; waits for them
+  // operand fragments of K slices 2h, 2h + 1 of step kstep (issued only; wait_lgkm0 waits for them)
   auto read_frags = [&](int kstep, int h) {
     const char* sa = lds + (kstep % T::A_STAGES) * T::OPB;
     const char* sb = lds + T::B_BASE + (kstep % T::B_STAGES) * T::OPB;
@@ -464,7 +458,6 @@ __device__ __attribute__((always_inline)) inline void pingpong_loop(char* lds, _
 #pragma unroll
       for (int i = 0; i < MI; ++i) af[h][s][i] = *(const bf16x8*)(sa + a_off + i * 32 * ROWB + coff);
     }
-    wait_lgkm0();
   };
   auto compute = [&](int h) {
 #pragma unroll
@@ -476,65 +469,40 @@ __device__ __attribute__((always_inline)) inline void pingpong_loop(char* lds, _
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[h][s][i], bfr[h][s][j], acc[i][j], 0, 0, 0);
   };
 
-  // prologue: this half's rows of A(0), B(0), B(1); wait for step 0
+  // prologue: this wave's rows of A(0), B(0), B(1); wait for step 0
   issue_a(0);
   issue_b(0);
   if (nk > 1) {
     issue_b(1);
-    wait_vmcnt<NL>();
+    wait_vmcnt<NL>();  // B loads are never skipped: the newest NL are step 1's
   } else {
     wait_vmcnt<0>();
   }
   bare_barrier();
-  // The two halves run separate straight-line loops (a wave's role never changes); both execute the
-  // same sequence of barriers, 4 per K step.
-  if (grp == 0) {
-    read_frags(0, 0);
-    if (nk > 1) issue_a(1);
-    bare_barrier();
-    for (int kt = 0; kt < nk; ++kt) {
-      compute(0);  // (kt, lo)
-      bare_barrier();
-      read_frags(kt, 1);
-      if (kt + 2 < nk) issue_b(kt + 2);
-      bare_barrier();
-      compute(1);  // (kt, hi)
-      // step kt + 1 has landed (only this wave's B loads of step kt + 2 may still be in flight)
+  for (int kt = 0; kt < nk; ++kt) {
+    // step kt is in LDS: A stage kt % 2, B stage kt % 3
+    read_frags(kt, 0);
+    wait_lgkm0();
+    if (kt + 1 < nk) issue_a(kt + 1);  // into the A stage step kt - 1 used (every wave is done with it)
+    read_frags(kt, 1);                 // lands while the lo half's MFMAs run
+    compute(0);
+    if (kt + 2 < nk) issue_b(kt + 2);  // into the B stage step kt - 1 used
+    wait_lgkm0();
+    compute(1);
+    // step kt + 1 has landed (only this wave's B loads of step kt + 2 may still be in flight)
+    if (kt + 1 < nk) {
       if (kt + 2 < nk)
         wait_vmcnt<NL>();
       else
         wait_vmcnt<0>();
-      bare_barrier();
-      if (kt + 1 < nk) {
-        read_frags(kt + 1, 0);
-        if (kt + 2 < nk) issue_a(kt + 2);
-      }
-      bare_barrier();
     }
-  } else {
     bare_barrier();
-    for (int kt = 0; kt < nk; ++kt) {
-      read_frags(kt, 0);
-      if (kt + 1 < nk) issue_a(kt + 1);
-      bare_barrier();
-      compute(0);  // (kt, lo)
-      bare_barrier();
-      read_frags(kt, 1);
-      if (kt + 2 < nk) issue_b(kt + 2);
-      if (kt + 2 < nk)
-        wait_vmcnt<NL>();
-      else
-        wait_vmcnt<0>();
-      bare_barrier();
-      compute(1);  // (kt, hi)
-      bare_barrier();
-    }
   }
 }
 
 template <bool GATE_UP>
-__global__ __launch_bounds__(512, 1) void grouped_bf16_pp(GroupedArgs a, int ncol_max) {
-  using T = PingPongTile<GATE_UP>;
+__global__ __launch_bounds__(512, 1) void grouped_bf16_w8(GroupedArgs a, int ncol_max) {
+  using T = Wave8Tile<GATE_UP>;
   constexpr int NL = T::NL, OC = T::OC;
   constexpr int OPITCH = OC + 8;  // bf16 per staged output row (16-byte pad)
   constexpr int OUT_BYTES = 8 * 64 * OPITCH * 2;
@@ -557,11 +525,7 @@ __global__ __launch_bounds__(512, 1) void grouped_bf16_pp(GroupedArgs a, int nco
 
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  // Waves 4-7 form half 0 (which computes first) and waves 0-3 half 1. Measured: LDS reads issued in
-  // a slot where the other wave of the SIMD still has MFMAs waiting for the matrix core come back
-  // slower for the younger wave of the pair, and half 1 reads in exactly those slots (4t, 4t + 2);
-  // handing them to the older waves cut the gate_up time by 4-5%.
-  const int grp = 1 - (wave >> 2), q = wave & 3;
+  const int grp = wave >> 2, q = wave & 3;
   const int m0 = grp * 128 + (q & 1) * 64, wn = q >> 1;
 
   // Direct-load sources: chunk p of this half's 128 rows is row 128 g + p / 8, slot p % 8, which holds
@@ -605,11 +569,11 @@ __global__ __launch_bounds__(512, 1) void grouped_bf16_pp(GroupedArgs a, int nco
   const int live_m = tile.rows - m0;
   const int mi = live_m <= 0 ? 0 : min(2, (live_m + 31) / 32);
   if (mi == 2)
-    pingpong_loop<GATE_UP, 2>(lds, rsrcA, offA, rsrcB, offB, acc, nk, grp, q, lane, m0, wn);
+    wave8_loop<GATE_UP, 2>(lds, rsrcA, offA, rsrcB, offB, acc, nk, grp, q, lane, m0, wn);
   else if (mi == 1)
-    pingpong_loop<GATE_UP, 1>(lds, rsrcA, offA, rsrcB, offB, acc, nk, grp, q, lane, m0, wn);
+    wave8_loop<GATE_UP, 1>(lds, rsrcA, offA, rsrcB, offB, acc, nk, grp, q, lane, m0, wn);
   else
-    pingpong_loop<GATE_UP, 0>(lds, rsrcA, offA, rsrcB, offB, acc, nk, grp, q, lane, m0, wn);
+    wave8_loop<GATE_UP, 0>(lds, rsrcA, offA, rsrcB, offB, acc, nk, grp, q, lane, m0, wn);
 
   // Epilogue through LDS (the loop ended on a barrier after the last operand read): each wave stages
   // its 64 x OC bf16 results (SwiGLU / weight scale applied) in its own padded region, then stores
@@ -652,8 +616,8 @@ __global__ __launch_bounds__(512, 1) void grouped_bf16_pp(GroupedArgs a, int nco
   }
 }
 
-#ifndef MOE_PF_PINGPONG
-#define MOE_PF_PINGPONG 1
+#ifndef MOE_PF_EIGHT_WAVES
+#define MOE_PF_EIGHT_WAVES 1
 #endif
 
 #ifndef MOE_PF_BK
@@ -663,9 +627,9 @@ __global__ __launch_bounds__(512, 1) void grouped_bf16_pp(GroupedArgs a, int nco
 #define MOE_PF_STAGES 2
 #endif
 
-// The ping-pong kernel addresses its operands with 32-bit byte offsets: from x for gathered rows,
+// The eight-wave kernel addresses its operands with 32-bit byte offsets: from x for gathered rows,
 // from a tile's first row otherwise, and from an expert's matrix for B.
-bool pingpong_fits(const GroupedArgs& a) {
+bool wave8_fits(const GroupedArgs& a) {
   constexpr int64_t LIM = int64_t(1) << 32;
   for (int p = 0; p < 2; ++p) {
     const ExpertProblem& P = a.prob[p];
@@ -686,8 +650,8 @@ hipError_t launch_bm(int bm, const GroupedArgs& a, int64_t max_tile_count, hipSt
   int64_t blocks = (max_tile_count * nc + 7) / 8 * 8;
   if (blocks == 0) return hipSuccess;
   if (bm != 256) return hipErrorInvalidValue;  // the forward builds 256-row tile lists for these kernels
-  if (MOE_PF_PINGPONG && pingpong_fits(a))
-    hipLaunchKernelGGL((grouped_bf16_pp<GATE_UP>), dim3((unsigned)blocks), dim3(512), 0, s, a, nc);
+  if (MOE_PF_EIGHT_WAVES && wave8_fits(a))
+    hipLaunchKernelGGL((grouped_bf16_w8<GATE_UP>), dim3((unsigned)blocks), dim3(512), 0, s, a, nc);
   else
     hipLaunchKernelGGL((grouped_bf16_lds<256, MOE_PF_BK, MOE_PF_STAGES, GATE_UP>), dim3((unsigned)blocks), dim3(256),
                        0, s, a, nc);
