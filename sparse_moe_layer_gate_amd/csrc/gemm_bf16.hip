@@ -368,10 +368,10 @@ __global__ __launch_bounds__(256, 1) void grouped_bf16_lds(GroupedArgs a, int nc
 //    and the matching 64 up rows, so SwiGLU pairs stay in one wave);
 //  - the waves of half g load rows [128 g, 128 g + 128) of both operands, four direct loads per lane
 //    of each per step (buffer_load_dwordx4 ... lds through raw buffer descriptors);
-//  - per K step t a wave reads the fragments of the step's first 32 K values, issues its A loads of
-//    step t + 1, reads the second half's fragments while the first half's MFMAs run, issues its B
-//    loads of step t + 2, runs the second half's MFMAs, waits for its loads of step t + 1 and meets
-//    the others at a barrier. A stage is refilled only after every wave has passed the barrier that
+//  - per K step t a wave issues its A loads of step t + 1, reads the fragments of the step's first 32
+//    K values, reads the second half's fragments while the first half's MFMAs run, issues its B loads
+//    of step t + 2, runs the second half's MFMAs, waits for its loads of step t + 1 and meets the
+//    others at a barrier. A stage is refilled only after every wave has passed the barrier that
 //    follows its last read; A loads get about one step to land and B loads two.
 template <bool GATE_UP>
 struct Wave8Tile {
@@ -481,9 +481,9 @@ __device__ __attribute__((always_inline)) inline void wave8_loop(char* lds, __am
   bare_barrier();
   for (int kt = 0; kt < nk; ++kt) {
     // step kt is in LDS: A stage kt % 2, B stage kt % 3
+    if (kt + 1 < nk) issue_a(kt + 1);  // into the A stage step kt - 1 used (every wave is done with it)
     read_frags(kt, 0);
     wait_lgkm0();
-    if (kt + 1 < nk) issue_a(kt + 1);  // into the A stage step kt - 1 used (every wave is done with it)
     read_frags(kt, 1);                 // lands while the lo half's MFMAs run
     compute(0);
     if (kt + 2 < nk) issue_b(kt + 2);  // into the B stage step kt - 1 used
