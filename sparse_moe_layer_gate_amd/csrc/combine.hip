@@ -12,19 +12,34 @@ namespace {
 
 constexpr int MAX_K = 32;
 
-__device__ inline void add8(float* acc, const uint16_t* p) {
-  const uint4 v = *(const uint4*)p;
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+// 8 consecutive elements of a row, as loaded
+template <typename T>
+struct V8;
+template <>
+struct V8<uint16_t> {
+  uint4 v;
+};
+template <>
+struct V8<float> {
+  float4 a, b;
+};
+__device__ inline V8<uint16_t> load8(const uint16_t* p) { return V8<uint16_t>{*(const uint4*)p}; }
+__device__ inline V8<float> load8(const float* p) { return V8<float>{*(const float4*)p, *(const float4*)(p + 4)}; }
+__device__ inline void add8(float* acc, const V8<uint16_t>& x) {
+  const uint32_t w[4] = {x.v.x, x.v.y, x.v.z, x.v.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     acc[2 * i] += __uint_as_float(w[i] << 16);
     acc[2 * i + 1] += __uint_as_float(w[i] & 0xffff0000u);
   }
 }
-__device__ inline void add8(float* acc, const float* p) {
-  const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
-  acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
-  acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+__device__ inline void add8(float* acc, const V8<float>& x) {
+  acc[0] += x.a.x; acc[1] += x.a.y; acc[2] += x.a.z; acc[3] += x.a.w;
+  acc[4] += x.b.x; acc[5] += x.b.y; acc[6] += x.b.z; acc[7] += x.b.w;
+}
+template <typename T>
+__device__ inline void add8(float* acc, const T* p) {
+  add8(acc, load8(p));
 }
 __device__ inline void store8(uint16_t* p, const float* acc) {
   uint4 v;
@@ -50,9 +65,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ Y, c
   __syncthreads();
   for (int c = threadIdx.x * 8; c < D; c += 256 * 8) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int slot = 0; slot < k; ++slot) {
-      const int r = rows[slot];
-      if (r >= 0) add8(acc, Y + (int64_t)r * D + c);
+    // slots in groups of 8: the group's row loads are all issued before the first add (a loop of
+    // load-then-add waited out one memory latency per slot); the adds keep slot order
+    for (int s0 = 0; s0 < k; s0 += 8) {
+      V8<T> v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int r = s0 + u < k ? rows[s0 + u] : -1;
+        if (r >= 0) v[u] = load8(Y + (int64_t)r * D + c);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (s0 + u < k && rows[s0 + u] >= 0) add8(acc, v[u]);
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = __fmul_rn(acc[i], alpha_out);  // exact when alpha_out == 1
