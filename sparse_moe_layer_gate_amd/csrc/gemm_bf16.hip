@@ -1,17 +1,21 @@
-// Grouped bf16 expert GEMMs for token-rich (prefill) batches.
+// Grouped bf16 expert GEMMs for token-rich (prefill) batches: 256-row tiles.
 //
 // Same products as the generic grouped kernels ("MoE Forward", eq. E_i: the gate_up GEMM with the
 // SwiGLU applied in registers, and the down GEMM scaled by the mixture weight w_{n,i}), laid out for
-// gfx950:
-//  - block tile BM x 256 with BM = 256 or 128, four waves; a wave owns (BM / WM) x (256 / WN) outputs
-//    as TM x TN tiles of v_mfma_f32_32x32x16_bf16 (accumulators in AGPRs);
-//  - operands go global -> LDS directly (global_load_lds_dwordx4: lane l of a wave writes bytes
-//    [16 l, 16 l + 16) of a 1 KiB run), no register staging;
+// gfx950. Two kernels:
+//  - grouped_bf16_w8 (the one the forward runs): eight waves, two per SIMD, each wave computing a
+//    64 x 128 share of a 256 x 256 tile and issuing an eighth of every step's loads (described where
+//    it is defined);
+//  - grouped_bf16_lds (fallback when x spans 4 GiB or more, where the eight-wave kernel's 32-bit
+//    buffer offsets do not reach): four waves, each 128 x 128 of the tile.
+// Common to both:
+//  - operands go global -> LDS directly (lane l of a wave writes bytes [16 l, 16 l + 16) of a 1 KiB
+//    run), no register staging;
 //  - LDS rows are BK bf16 long, unpadded; the 16-byte chunks of a row are XOR-swizzled by the row's
 //    position so that the MFMA operand reads (32 rows at one k offset) hit distinct banks;
-//  - STAGES-deep ring of K steps: loads for step t + STAGES - 1 are in flight while step t computes;
-//  - 32-row MFMA sub-tiles past a tile's valid rows are skipped, so a sparsely filled tile (a rarely
-//    chosen expert) costs little MFMA time.
+//  - v_mfma_f32_32x32x16_bf16 tiles; 32-row MFMA sub-tiles past a tile's valid rows are skipped, so a
+//    sparsely filled tile (a rarely chosen expert) costs little MFMA time;
+//  - blocks follow an XCD-aware order over the valid tiles with a row-tile-major rasterization.
 #include <hip/hip_runtime.h>
 
 #include "moe_internal.h"
