@@ -31,17 +31,6 @@ __global__ __launch_bounds__(256) void count_kernel(const int32_t* __restrict__ 
   for (int e = threadIdx.x; e < E; e += 256) chunk_counts[(int64_t)c * E + e] = hist[e];
 }
 
-__device__ void write_tiles(const TileSpec& ts, int e, int count, int offset, int first_tile) {
-  for (int j = 0; j * ts.bm < count; ++j) {
-    Tile t;
-    t.problem = 0;
-    t.expert = e;
-    t.row_start = offset + j * ts.bm;
-    t.rows = min(ts.bm, count - j * ts.bm);
-    ts.tiles[first_tile + j] = t;
-  }
-}
-
 // Exclusive scan of one int per thread over a 512-thread block (8 waves): shuffles inside each wave,
 // then the wave totals. Returns the exclusive prefix; *total receives the block sum.
 __device__ int block_exclusive_scan(int v, int* wsum, int* total) {
@@ -65,17 +54,45 @@ __device__ int block_exclusive_scan(int v, int* wsum, int* total) {
   return before + incl - v;
 }
 
-__device__ void write_shared_tiles(const TileSpec& ts, int routed_tiles, int64_t N, int n_shared_problem) {
-  const int64_t nsh = n_shared_problem ? (N + ts.bm - 1) / ts.bm : 0;
-  for (int64_t j = threadIdx.x; j < nsh; j += blockDim.x) {
-    Tile t;
-    t.problem = 1;
-    t.expert = 0;
-    t.row_start = (int)(j * ts.bm);
-    t.rows = (int)min((int64_t)ts.bm, N - j * ts.bm);
-    ts.tiles[routed_tiles + j] = t;
+// Position in the merged list of the i-th small-expert tile (a) and of the j-th other tile (b), with na
+// and nb tiles in the two classes. The merge orders a tile by its fractional rank ((2 i + 1) / (2 na)
+// or (2 j + 1) / (2 nb); a before b on equal ranks), so every stretch of the list holds the two classes
+// in the same proportion.
+__device__ inline int merged_pos_a(int i, int na, int nb) {
+  const int64_t c = ((int64_t)(2 * i + 1) * nb + na - 1) / na;  // ceil
+  return i + (int)min((int64_t)nb, c / 2);
+}
+__device__ inline int merged_pos_b(int j, int na, int nb) {
+  if (na == 0) return j;
+  const int64_t f = (int64_t)(2 * j + 1) * na / nb;  // floor
+  return j + (int)min((int64_t)na, (f + 1) / 2);
+}
+
+// Row-tile list of one grouped GEMM (called by every thread of the scan block; thread e < E holds
+// expert e's count and row offset). Order: the routed experts' tiles in expert order, then the shared
+// expert's, except that with ts.small_max > 0 the single tiles of experts with 1..small_max rows are
+// taken out and merged back evenly (merged_pos_*): the grouped kernels hand each XCD a contiguous run
+// of the list, and the merge gives every run the same mix of full tiles and nearly empty ones. An
+// expert's tiles stay together either way, so row tiles that share its weights still meet in one L2.
+__device__ void build_tiles(const TileSpec& ts, bool valid, int e, int cnt, int off, int64_t N,
+                            int n_shared_problem, int* wsum) {
+  const int nt = valid ? (cnt + ts.bm - 1) / ts.bm : 0;
+  const bool small = valid && cnt >= 1 && cnt <= ts.small_max && cnt <= ts.bm;
+  int na, nrouted;
+  const int ia = block_exclusive_scan(small ? 1 : 0, wsum, &na);
+  const int ib = block_exclusive_scan(small ? 0 : nt, wsum, &nrouted);
+  const int nsh = n_shared_problem ? (int)((N + ts.bm - 1) / ts.bm) : 0;
+  const int nb = nrouted + nsh;
+  if (small) {
+    ts.tiles[merged_pos_a(ia, na, nb)] = Tile{0, e, off, cnt};
+  } else {
+    for (int j = 0; j < nt; ++j)
+      ts.tiles[merged_pos_b(ib + j, na, nb)] = Tile{0, e, off + j * ts.bm, min(ts.bm, cnt - j * ts.bm)};
   }
-  if (threadIdx.x == 0) *ts.n_tiles = routed_tiles + (int)nsh;
+  for (int j = threadIdx.x; j < nsh; j += blockDim.x)
+    ts.tiles[merged_pos_b(nrouted + j, na, nb)] =
+        Tile{1, 0, j * ts.bm, (int)min((int64_t)ts.bm, N - (int64_t)j * ts.bm)};
+  if (threadIdx.x == 0) *ts.n_tiles = na + nb;
 }
 
 __global__ __launch_bounds__(512) void scan_kernel(const int32_t* __restrict__ chunk_counts, int nchunks, int64_t N,
@@ -99,23 +116,17 @@ __global__ __launch_bounds__(512) void scan_kernel(const int32_t* __restrict__ c
       }
     }
   }
-  const int nt0 = e < E ? (cnt + t0.bm - 1) / t0.bm : 0;
-  const int nt1 = e < E ? (cnt + t1.bm - 1) / t1.bm : 0;
-  int total, tiles0, tiles1;
+  int total;
   const int off = block_exclusive_scan(cnt, wsum, &total);
-  const int toff0 = block_exclusive_scan(nt0, wsum, &tiles0);
-  const int toff1 = block_exclusive_scan(nt1, wsum, &tiles1);
   if (e < E) {
     counts[e] = cnt;
     offsets[e] = off;
     for (int c = 0; c < nchunks; ++c) chunk_base[(int64_t)c * E + e] += off;
-    write_tiles(t0, e, cnt, off, toff0);
-    write_tiles(t1, e, cnt, off, toff1);
   }
   if (e == 0) offsets[E] = total;
-  // the shared expert's tiles follow the routed ones: all N tokens, in token order
-  write_shared_tiles(t0, tiles0, N, n_shared_problem);
-  write_shared_tiles(t1, tiles1, N, n_shared_problem);
+  // the shared expert's tiles cover all N tokens, in token order
+  build_tiles(t0, e < E, e, cnt, off, N, n_shared_problem, wsum);
+  build_tiles(t1, e < E, e, cnt, off, N, n_shared_problem, wsum);
 }
 
 // Stable placement of one chunk: rounds of 256 pairs (in pair order); inside a round, a pair's

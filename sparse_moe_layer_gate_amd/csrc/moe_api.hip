@@ -193,8 +193,8 @@ moe_status dispatch_impl(const moe_config* c, int64_t N, const int32_t* idx, int
   const int E = c->n_routed_experts, k = c->num_experts_per_tok;
   const int nchunks = (int)((N + kDispatchChunk - 1) / kDispatchChunk);
   int32_t* ntiles = at<int32_t>(ws, L.ntiles);
-  TileSpec t0{L.bm0, at<Tile>(ws, L.tiles0), ntiles};
-  TileSpec t1{L.bm1, at<Tile>(ws, L.tiles1), ntiles + 1};
+  TileSpec t0{L.bm0, at<Tile>(ws, L.tiles0), ntiles, small_expert_rows(c->dtype, L.bm0)};
+  TileSpec t1{L.bm1, at<Tile>(ws, L.tiles1), ntiles + 1, small_expert_rows(c->dtype, L.bm1)};
   MOE_TRY(ST_COUNT, launch_count(idx, N, k, E, at<int32_t>(ws, L.chunk_counts), s));
   MOE_TRY(ST_SCAN, launch_scan(at<int32_t>(ws, L.chunk_counts), nchunks, N, k, E, c->n_shared_experts > 0, counts,
                                offsets, at<int32_t>(ws, L.chunk_base), t0, t1, s));
@@ -399,8 +399,8 @@ moe_status moe_dense_forward(int64_t N, int32_t D, int32_t dff, int32_t dtype, f
   hipStream_t s = (hipStream_t)stream;
   void* ws = workspace;
   int32_t* ntiles = at<int32_t>(ws, L.ntiles);
-  TileSpec t0{L.bm, at<Tile>(ws, L.tiles0), ntiles};
-  TileSpec t1{L.bm, at<Tile>(ws, L.tiles1), ntiles + 1};
+  TileSpec t0{L.bm, at<Tile>(ws, L.tiles0), ntiles, 0};
+  TileSpec t1{L.bm, at<Tile>(ws, L.tiles1), ntiles + 1, 0};
   if (launch_dense_tiles(N, t0, t1, s) != hipSuccess) return MOE_ERR_HIP;
   // one dense problem through the grouped GEMMs: no gather, no row scale; offsets = nullptr marks it
   // as a large problem for the prefill kernel's loop choice

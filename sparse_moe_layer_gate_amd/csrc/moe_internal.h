@@ -83,6 +83,7 @@ struct TileSpec {
   int bm;            // rows per tile
   Tile* tiles;       // output list
   int32_t* n_tiles;  // output count
+  int small_max;     // > 0: tiles of experts with 1..small_max rows are spread evenly among the others
 };
 hipError_t launch_count(const int32_t* idx, int64_t N, int k, int E, int32_t* chunk_counts, hipStream_t s);
 hipError_t launch_scan(const int32_t* chunk_counts, int nchunks, int64_t N, int k, int E, int n_shared_problem,
@@ -155,6 +156,7 @@ __device__ inline int64_t xcd_logical_block(int64_t nvalid) {
 // Upper bound on tiles for a tile list with bm rows per tile.
 int64_t max_tiles(int64_t N, int k, int E, int n_shared_problem, int bm);
 int gemm_bm(int dtype, int64_t N, int k, int E);  // rows per tile the forward will use
+int small_expert_rows(int dtype, int bm);         // TileSpec::small_max for a list of bm-row tiles
 hipError_t launch_gate_up(int dtype, const GroupedArgs& a, int64_t max_tile_count, hipStream_t s);
 hipError_t launch_down(int dtype, const GroupedArgs& a, int64_t max_tile_count, hipStream_t s);
 hipError_t launch_bf16_prefill(bool gate_up, int bm, const GroupedArgs& a, int64_t max_tile_count, hipStream_t s);
