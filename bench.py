@@ -36,7 +36,8 @@ HBM = 8.0e12  # B/s
 METRIC = "MoE-layer tokens/s + % bf16 MFMA peak (prefill), % HBM BW (decode)"
 DOMINANT = "experts_gate_up"
 KERNEL_SOURCES = ["sparse_moe_layer_gate_amd/csrc/gemm_bf16.hip", "sparse_moe_layer_gate_amd/csrc/gemm_decode.hip",
-                  "sparse_moe_layer_gate_amd/csrc/moe_internal.h"]
+                  "sparse_moe_layer_gate_amd/csrc/gemm.hip", "sparse_moe_layer_gate_amd/csrc/dispatch.hip",
+                  "sparse_moe_layer_gate_amd/csrc/moe_internal.h"]  # kernels, launch choice, tile lists
 
 
 def kernel_source_hash() -> str:

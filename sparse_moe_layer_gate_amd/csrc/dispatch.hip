@@ -58,14 +58,18 @@ __device__ int block_exclusive_scan(int v, int* wsum, int* total) {
 // and nb tiles in the two classes. The merge orders a tile by its fractional rank ((2 i + 1) / (2 na)
 // or (2 j + 1) / (2 nb); a before b on equal ranks), so every stretch of the list holds the two classes
 // in the same proportion.
+// Quotient of p / q for q > 0, in 32 bits when p fits (a 64-bit division is a long emulated sequence).
+__device__ inline uint64_t udiv(uint64_t p, uint32_t q) {
+  return p <= 0xffffffffull ? (uint64_t)((uint32_t)p / q) : p / q;
+}
 __device__ inline int merged_pos_a(int i, int na, int nb) {
-  const int64_t c = ((int64_t)(2 * i + 1) * nb + na - 1) / na;  // ceil
-  return i + (int)min((int64_t)nb, c / 2);
+  const uint64_t c = udiv((uint64_t)(2 * i + 1) * nb + na - 1, na);  // ceil
+  return i + (int)min((uint64_t)nb, c / 2);
 }
 __device__ inline int merged_pos_b(int j, int na, int nb) {
   if (na == 0) return j;
-  const int64_t f = (int64_t)(2 * j + 1) * na / nb;  // floor
-  return j + (int)min((int64_t)na, (f + 1) / 2);
+  const uint64_t f = udiv((uint64_t)(2 * j + 1) * na, nb);  // floor
+  return j + (int)min((uint64_t)na, (f + 1) / 2);
 }
 
 // Row-tile list of one grouped GEMM (called by every thread of the scan block; thread e < E holds
@@ -101,19 +105,14 @@ __global__ __launch_bounds__(512) void scan_kernel(const int32_t* __restrict__ c
                                                    TileSpec t0, TileSpec t1) {
   __shared__ int wsum[8];
   const int e = threadIdx.x;
-  // per expert: exclusive scan over chunks (chunk bases before the expert offset is known)
+  // per expert: its total over the chunks, then (once the expert offsets are known) the chunk bases;
+  // eight independent loads in flight per round in both passes (a serial chain of loads, or a
+  // read-modify-write pass over chunk_base, costs ~1 us per chunk)
   int cnt = 0;
   if (e < E) {
-    // eight independent loads in flight per round (a serial chain of loads took ~1 us per chunk)
     for (int c0 = 0; c0 < nchunks; c0 += 8) {
-      int v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = c0 + u < nchunks ? chunk_counts[(int64_t)(c0 + u) * E + e] : 0;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (c0 + u < nchunks) chunk_base[(int64_t)(c0 + u) * E + e] = cnt;
-        cnt += v[u];
-      }
+      for (int u = 0; u < 8; ++u) cnt += c0 + u < nchunks ? chunk_counts[(int64_t)(c0 + u) * E + e] : 0;
     }
   }
   int total;
@@ -121,7 +120,17 @@ __global__ __launch_bounds__(512) void scan_kernel(const int32_t* __restrict__ c
   if (e < E) {
     counts[e] = cnt;
     offsets[e] = off;
-    for (int c = 0; c < nchunks; ++c) chunk_base[(int64_t)c * E + e] += off;
+    int run = off;
+    for (int c0 = 0; c0 < nchunks; c0 += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = c0 + u < nchunks ? chunk_counts[(int64_t)(c0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (c0 + u < nchunks) chunk_base[(int64_t)(c0 + u) * E + e] = run;
+        run += v[u];
+      }
+    }
   }
   if (e == 0) offsets[E] = total;
   // the shared expert's tiles cover all N tokens, in token order
