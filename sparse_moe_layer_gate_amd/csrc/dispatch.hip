@@ -97,6 +97,7 @@ __device__ void build_tiles(const TileSpec& ts, bool valid, int e, int cnt, int 
     ts.tiles[merged_pos_b(nrouted + j, na, nb)] =
         Tile{1, 0, j * ts.bm, (int)min((int64_t)ts.bm, N - (int64_t)j * ts.bm)};
   if (threadIdx.x == 0) *ts.n_tiles = na + nb;
+  if (ts.work_ctr && threadIdx.x < 8) ts.work_ctr[threadIdx.x] = 0;
 }
 
 __global__ __launch_bounds__(512) void scan_kernel(const int32_t* __restrict__ chunk_counts, int nchunks, int64_t N,
@@ -201,6 +202,7 @@ __global__ __launch_bounds__(256) void dense_tiles_kernel(int64_t N, TileSpec t0
       ts.tiles[j] = t;
     }
     if (blockIdx.x == 0 && threadIdx.x == 0) *ts.n_tiles = (int)nt;
+    if (blockIdx.x == 0 && threadIdx.x < 8 && ts.work_ctr) ts.work_ctr[threadIdx.x] = 0;
   }
 }
 

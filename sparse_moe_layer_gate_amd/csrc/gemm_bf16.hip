@@ -504,19 +504,17 @@ __device__ __attribute__((always_inline)) inline void wave8_loop(char* lds, __am
   }
 }
 
+// One logical block of the eight-wave kernel: row tile and column tile from the logical id L, K loop,
+// epilogue. Every wave of the block calls it with the same arguments.
 template <bool GATE_UP>
-__global__ __launch_bounds__(512, 1) void grouped_bf16_w8(GroupedArgs a, int ncol_max) {
+__device__ __forceinline__ void w8_block(const GroupedArgs& a, int ncol_max, int64_t n_tiles, int64_t L, char* lds) {
   using T = Wave8Tile<GATE_UP>;
   constexpr int NL = T::NL, OC = T::OC;
   constexpr int OPITCH = OC + 8;  // bf16 per staged output row (16-byte pad)
   constexpr int OUT_BYTES = 8 * 64 * OPITCH * 2;
   constexpr int WROW_OFF = OUT_BYTES;  // row scales (down), after the staged outputs
   static_assert(T::RING <= 160 * 1024 && WROW_OFF + 256 * 4 <= T::RING, "LDS budget");
-  __shared__ __attribute__((aligned(1024))) char lds[T::RING];
 
-  const int64_t n_tiles = *a.n_tiles;
-  const int64_t L = xcd_logical_block(n_tiles * ncol_max);
-  if (L < 0) return;
   constexpr int GR = GATE_UP ? MOE_PF_GROUP_ROWS_GU : MOE_PF_GROUP_ROWS_DN;
   const int64_t sg = L / ((int64_t)GR * ncol_max), within = L % ((int64_t)GR * ncol_max);
   const int64_t gr = min((int64_t)GR, n_tiles - sg * GR);
@@ -620,6 +618,38 @@ __global__ __launch_bounds__(512, 1) void grouped_bf16_w8(GroupedArgs a, int nco
   }
 }
 
+// Persistent form: one block per CU. The logical blocks are split into 8 contiguous runs of nearly equal
+// length, one per XCD (the run the hardware's round-robin deal of a full grid would give that XCD,
+// xcd_logical_block), and a block claims the next logical block of its XCD's run from that run's
+// counter; when the run is empty it claims from the other runs in turn, and it exits once all eight
+// are empty. Compared with one launched block per logical block this removes the gaps between
+// consecutive blocks on a CU (the dispatcher deals workgroups in order, so a busy XCD holds up the
+// next workgroup of every other XCD) and lets the XCDs that finish early take the others' last blocks.
+template <bool GATE_UP>
+__global__ __launch_bounds__(512, 1) void grouped_bf16_w8(GroupedArgs a, int ncol_max) {
+  constexpr int RING = Wave8Tile<GATE_UP>::RING;
+  __shared__ __attribute__((aligned(1024))) char lds[RING];
+  // The claimed index passes through the ring's last word: the K loop is over when it is written (the
+  // epilogue's barrier) and the epilogue stages below it; the next K loop starts after every wave read it.
+  static_assert(8 * 64 * (Wave8Tile<GATE_UP>::OC + 8) * 2 + 256 * 4 <= RING - 4, "claim word overlaps the epilogue");
+  int* claim_word = (int*)(lds + RING - 4);
+  const int64_t n_tiles = *a.n_tiles, nvalid = n_tiles * ncol_max;
+  const int64_t q = nvalid >> 3, r = nvalid & 7;
+  const int x = blockIdx.x & 7;  // the XCD the hardware dealt this block to
+  for (int v = 0; v < 8; ++v) {
+    const int y = (x + v) & 7;
+    const int64_t start = y * q + min((int64_t)y, r), len = q + (y < r ? 1 : 0);
+    for (;;) {
+      if (threadIdx.x == 0) *claim_word = atomicAdd(&a.work_ctr[y], 1);
+      __syncthreads();  // also: the previous logical block's epilogue is done with the LDS
+      const int64_t j = *claim_word;
+      __syncthreads();  // every wave has read claim before it is overwritten
+      if (j >= len) break;
+      w8_block<GATE_UP>(a, ncol_max, n_tiles, start + j, lds);
+    }
+  }
+}
+
 #ifndef MOE_PF_EIGHT_WAVES
 #define MOE_PF_EIGHT_WAVES 1
 #endif
@@ -645,6 +675,20 @@ bool wave8_fits(const GroupedArgs& a) {
   return true;
 }
 
+// Blocks of the persistent kernel: one per CU of the current device (a multiple of 8: every XCD gets
+// the same number), queried once per device.
+int64_t persistent_grid() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8) n = 256;
+    cached[dev] = n / 8 * 8;
+  }
+  return cached[dev];
+}
+
 template <bool GATE_UP>
 hipError_t launch_bm(int bm, const GroupedArgs& a, int64_t max_tile_count, hipStream_t s) {
   constexpr int COLS = GATE_UP ? 128 : 256;
@@ -654,9 +698,11 @@ hipError_t launch_bm(int bm, const GroupedArgs& a, int64_t max_tile_count, hipSt
   int64_t blocks = (max_tile_count * nc + 7) / 8 * 8;
   if (blocks == 0) return hipSuccess;
   if (bm != 256) return hipErrorInvalidValue;  // the forward builds 256-row tile lists for these kernels
-  if (MOE_PF_EIGHT_WAVES && wave8_fits(a))
-    hipLaunchKernelGGL((grouped_bf16_w8<GATE_UP>), dim3((unsigned)blocks), dim3(512), 0, s, a, nc);
-  else
+  if (MOE_PF_EIGHT_WAVES && wave8_fits(a)) {
+    if (!a.work_ctr) return hipErrorInvalidValue;
+    const int64_t grid = min(blocks, persistent_grid());
+    hipLaunchKernelGGL((grouped_bf16_w8<GATE_UP>), dim3((unsigned)grid), dim3(512), 0, s, a, nc);
+  } else
     hipLaunchKernelGGL((grouped_bf16_lds<256, MOE_PF_BK, MOE_PF_STAGES, GATE_UP>), dim3((unsigned)blocks), dim3(256),
                        0, s, a, nc);
   return hipGetLastError();

@@ -85,7 +85,7 @@ Workspace layout(const moe_config* c, int64_t N) {
   w.inv_row = take(sizeof(int32_t) * N * k);
   w.tiles0 = take(sizeof(Tile) * w.max_tiles0);
   w.tiles1 = take(sizeof(Tile) * w.max_tiles1);
-  w.ntiles = take(sizeof(int32_t) * 2);
+  w.ntiles = take(sizeof(int32_t) * 18);  // two tile counts, 8 work counters per list
   w.H = take(es * N * k * d);
   w.Hsh = take(es * N * dsh);
   w.Y = take(es * N * k * D);
@@ -114,7 +114,7 @@ DenseWorkspace dense_layout(int64_t N, int dff, int dtype) {
   };
   w.tiles0 = take(sizeof(Tile) * w.max_tiles);
   w.tiles1 = take(sizeof(Tile) * w.max_tiles);
-  w.ntiles = take(sizeof(int32_t) * 2);
+  w.ntiles = take(sizeof(int32_t) * 18);  // two tile counts, 8 work counters per list
   w.H = take(es * N * dff);
   w.total = o;
   return w;
@@ -193,8 +193,8 @@ moe_status dispatch_impl(const moe_config* c, int64_t N, const int32_t* idx, int
   const int E = c->n_routed_experts, k = c->num_experts_per_tok;
   const int nchunks = (int)((N + kDispatchChunk - 1) / kDispatchChunk);
   int32_t* ntiles = at<int32_t>(ws, L.ntiles);
-  TileSpec t0{L.bm0, at<Tile>(ws, L.tiles0), ntiles, small_expert_rows(c->dtype, L.bm0)};
-  TileSpec t1{L.bm1, at<Tile>(ws, L.tiles1), ntiles + 1, small_expert_rows(c->dtype, L.bm1)};
+  TileSpec t0{L.bm0, at<Tile>(ws, L.tiles0), ntiles, small_expert_rows(c->dtype, L.bm0), ntiles + 2};
+  TileSpec t1{L.bm1, at<Tile>(ws, L.tiles1), ntiles + 1, small_expert_rows(c->dtype, L.bm1), ntiles + 10};
   MOE_TRY(ST_COUNT, launch_count(idx, N, k, E, at<int32_t>(ws, L.chunk_counts), s));
   MOE_TRY(ST_SCAN, launch_scan(at<int32_t>(ws, L.chunk_counts), nchunks, N, k, E, c->n_shared_experts > 0, counts,
                                offsets, at<int32_t>(ws, L.chunk_base), t0, t1, s));
@@ -219,6 +219,7 @@ moe_status experts_impl(const moe_config* cfg, int64_t N, const void* x, const m
   // gate_up + SwiGLU: routed rows gather x through sorted_pair; the shared expert reads x in order
   g.tiles = at<Tile>(ws, L.tiles0);
   g.n_tiles = at<int32_t>(ws, L.ntiles);
+  g.work_ctr = at<int32_t>(ws, L.ntiles) + 2;
   g.bm = L.bm0;
   g.prob[0] = ExpertProblem{x, D, 1, wt->gate_up, (const char*)wt->gate_up + es * (int64_t)d * D, 2LL * d * D, D, d,
                             at<void>(ws, L.H), d, 0};
@@ -228,6 +229,7 @@ moe_status experts_impl(const moe_config* cfg, int64_t N, const void* x, const m
   // down + mixture weight (routed) / weight 1 (shared)
   g.tiles = at<Tile>(ws, L.tiles1);
   g.n_tiles = at<int32_t>(ws, L.ntiles) + 1;
+  g.work_ctr = at<int32_t>(ws, L.ntiles) + 10;
   g.bm = L.bm1;
   g.prob[0] = ExpertProblem{at<void>(ws, L.H), d, 0, wt->down, nullptr, (int64_t)D * d, d, D, at<void>(ws, L.Y), D, 1};
   if (shared)
@@ -399,8 +401,8 @@ moe_status moe_dense_forward(int64_t N, int32_t D, int32_t dff, int32_t dtype, f
   hipStream_t s = (hipStream_t)stream;
   void* ws = workspace;
   int32_t* ntiles = at<int32_t>(ws, L.ntiles);
-  TileSpec t0{L.bm, at<Tile>(ws, L.tiles0), ntiles, 0};
-  TileSpec t1{L.bm, at<Tile>(ws, L.tiles1), ntiles + 1, 0};
+  TileSpec t0{L.bm, at<Tile>(ws, L.tiles0), ntiles, 0, ntiles + 2};
+  TileSpec t1{L.bm, at<Tile>(ws, L.tiles1), ntiles + 1, 0, ntiles + 10};
   if (launch_dense_tiles(N, t0, t1, s) != hipSuccess) return MOE_ERR_HIP;
   // one dense problem through the grouped GEMMs: no gather, no row scale; offsets = nullptr marks it
   // as a large problem for the prefill kernel's loop choice
@@ -409,11 +411,13 @@ moe_status moe_dense_forward(int64_t N, int32_t D, int32_t dff, int32_t dtype, f
   g.swiglu_limit = swiglu_limit;
   g.tiles = t0.tiles;
   g.n_tiles = ntiles;
+  g.work_ctr = t0.work_ctr;
   g.bm = L.bm;
   g.prob[0] = ExpertProblem{x, D, 0, gate, up, 0, D, dff, at<void>(ws, L.H), dff, 0};
   MOE_TRY(ST_GATE_UP, launch_gate_up(dtype, g, L.max_tiles, s));
   g.tiles = t1.tiles;
   g.n_tiles = ntiles + 1;
+  g.work_ctr = t1.work_ctr;
   g.prob[0] = ExpertProblem{at<void>(ws, L.H), dff, 0, down, nullptr, 0, dff, D, y, D, 0};
   MOE_TRY(ST_DOWN, launch_down(dtype, g, L.max_tiles, s));
   return MOE_OK;

@@ -84,6 +84,7 @@ struct TileSpec {
   Tile* tiles;       // output list
   int32_t* n_tiles;  // output count
   int small_max;     // > 0: tiles of experts with 1..small_max rows are spread evenly among the others
+  int32_t* work_ctr;  // the list's 8 work counters (persistent kernels), zeroed with the list; or nullptr
 };
 hipError_t launch_count(const int32_t* idx, int64_t N, int k, int E, int32_t* chunk_counts, hipStream_t s);
 hipError_t launch_scan(const int32_t* chunk_counts, int nchunks, int64_t N, int k, int E, int n_shared_problem,
@@ -119,6 +120,7 @@ struct GroupedArgs {
   const int32_t* offsets;  // routed experts' row offsets [E + 1] (or nullptr: every expert counts as large)
   float swiglu_limit;      // gate_up epilogue clamp bound (0: plain SwiGLU)
   int64_t gather_rows;     // rows of the matrix that gathered A rows index (x); 0 when unknown
+  int32_t* work_ctr;       // 8 counters, zero at launch: per-XCD work claims of the persistent kernels
 };
 // Field-wise select keeps a problem descriptor in scalar registers (a dynamically indexed
 // kernel-argument array would be copied to scratch).
