@@ -5,7 +5,7 @@
 // gfx950. Two kernels:
 //  - grouped_bf16_w8 (the one the forward runs): eight waves, two per SIMD, each wave computing a
 //    64 x 128 share of a 256 x 256 tile and issuing an eighth of every step's loads (described where
-//    it is defined);
+//    it is defined); persistent, one block per CU claiming tiles per XCD;
 //  - grouped_bf16_lds (fallback when x spans 4 GiB or more, where the eight-wave kernel's 32-bit
 //    buffer offsets do not reach): four waves, each 128 x 128 of the tile.
 // Common to both:
