@@ -334,7 +334,7 @@ __global__ __launch_bounds__(256, 1) void grouped_bf16_lds(GroupedArgs a, int nc
       if (GATE_UP) {
 #pragma unroll
         for (int j = 0; j < TN / 2; ++j)
-          stage_out[row * OPITCH + j * 32 + (lane & 31)] = bf16_rne(swiglu(acc[i][j][r], acc[i][j + TN / 2][r], a.swiglu_limit));
+          stage_out[row * OPITCH + j * 32 + (lane & 31)] = bf16_rne(swiglu_bf16(acc[i][j][r], acc[i][j + TN / 2][r], a.swiglu_limit));
       } else {
         const float sc = wrow[min(wm * WAVE_M + row, BM - 1)];
 #pragma unroll
@@ -595,7 +595,7 @@ __device__ __forceinline__ void w8_block(const GroupedArgs& a, int ncol_max, int
       if (GATE_UP) {
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          stage_out[row * OPITCH + j * 32 + (lane & 31)] = bf16_rne(swiglu(acc[i][j][r], acc[i][j + 2][r], a.swiglu_limit));
+          stage_out[row * OPITCH + j * 32 + (lane & 31)] = bf16_rne(swiglu_bf16(acc[i][j][r], acc[i][j + 2][r], a.swiglu_limit));
       } else {
         const float sc = wrow[m0 + row];
 #pragma unroll

@@ -168,7 +168,7 @@ __global__ __launch_bounds__(256) void grouped_bf16_decode(GroupedArgs a, int nc
 #pragma unroll
       for (int j = 0; j < NT / 2; ++j) {
         const int col = wcol0 + j * 16 + r16;
-        if (col < P.ncols) out[orow * P.ldo + col] = bf16_rne(swiglu(acc[j][i], acc[j + NT / 2][i], a.swiglu_limit));
+        if (col < P.ncols) out[orow * P.ldo + col] = bf16_rne(swiglu_bf16(acc[j][i], acc[j + NT / 2][i], a.swiglu_limit));
       }
     } else {
       const float sc = P.scale_rows ? a.topk_w[a.sorted_pair[orow]] : 1.0f;

@@ -50,6 +50,15 @@ __device__ inline float swiglu(float g, float u, float lim) {
   }
   return g / (1.0f + expf(-g)) * u;
 }
+// The same for results rounded to bfloat16: the hardware exponential and reciprocal (a few float32 ulp,
+// far below the bfloat16 rounding that follows) instead of the full-precision library sequence.
+__device__ inline float swiglu_bf16(float g, float u, float lim) {
+  if (lim > 0.f) {
+    g = fminf(g, lim);
+    u = fminf(fmaxf(u, -lim), lim);
+  }
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
 
 // s_waitcnt with vmcnt = N and the other counters left at their maximum (gfx9 encoding).
 template <int N>
