@@ -59,6 +59,50 @@ __device__ inline int rb_swz(int r) {
   return ((r >> 1) ^ (r >> 3)) & 3;
 }
 
+// The K loop of one wave with NJ of its two 32-expert column tiles inside E (column tiles past E, as in
+// the last block column when E is not a multiple of 128, issue no MFMAs). Every wave runs the same
+// loads and barriers whatever its NJ.
+template <int NJ>
+__device__ __forceinline__ void rb_loop(char* lds, const uint16_t* srcA, const uint16_t* const (&srcB)[RB_NB],
+                                        uint32_t bmask, int nk, int wave, int lane, int wm, int wn, f32x16 (&acc)[2]) {
+  auto issue = [&](int kstep) {
+    char* st = lds + (kstep & 1) * RB_STAGE;
+    const int k0 = kstep * RB_BK;
+    __builtin_amdgcn_global_load_lds((const void*)(srcA + k0), (lds_void*)(st + wave * 1024), 16, 0, 0);
+#pragma unroll
+    for (int q = 0; q < RB_NB; ++q)
+      if (bmask & (1u << q))  // rows of experts past E are not loaded (nothing reads them)
+        __builtin_amdgcn_global_load_lds((const void*)(srcB[q] + k0),
+                                         (lds_void*)(st + RB_A_BYTES + (q * 4 + wave) * 1024), 16, 0, 0);
+  };
+  const int sw = rb_swz(lane & 31);
+  const int a_off = (wm * 32 + (lane & 31)) * RB_ROWB;
+  if (nk > 0) issue(0);
+  for (int kt = 0; kt < nk; ++kt) {
+    // this wave's loads for step kt are complete; after the barrier everyone's are, and every read of
+    // the stage refilled next (step kt - 1) is done
+    wait_vmcnt<0>();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (kt + 1 < nk) issue(kt + 1);
+    const char* st = lds + (kt & 1) * RB_STAGE;
+#pragma unroll
+    for (int kk = 0; kk < RB_BK / 16; ++kk) {
+      const int coff = ((2 * kk + (lane >> 5)) ^ sw) * 16;
+      const bf16x8 af = *(const bf16x8*)(st + a_off + coff);
+#pragma unroll
+      for (int piece = 2; piece >= 0; --piece)  // smallest piece first
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int brow = piece * RB_BN + wn * 64 + j * 32 + (lane & 31);
+          const bf16x8 bf = *(const bf16x8*)(st + RB_A_BYTES + brow * RB_ROWB + coff);
+          acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc[j], 0, 0, 0);
+        }
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void logits_bf16x3_kernel(const uint16_t* __restrict__ x,
                                                             const uint16_t* __restrict__ w3, int64_t N, int D, int E,
                                                             int kchunk, float* __restrict__ part) {
@@ -79,6 +123,7 @@ __global__ __launch_bounds__(256) void logits_bf16x3_kernel(const uint16_t* __re
     srcA = x + n * D + kbeg + 8 * c;
   }
   const uint16_t* srcB[RB_NB];
+  uint32_t bmask = 0;
 #pragma unroll
   for (int q = 0; q < RB_NB; ++q) {
     const int p = (q * 4 + wave) * 64 + lane;
@@ -86,49 +131,22 @@ __global__ __launch_bounds__(256) void logits_bf16x3_kernel(const uint16_t* __re
     const int c = (p % RB_CPR) ^ rb_swz(rr);
     const int e = min(e0 + rr, E - 1);
     srcB[q] = w3 + (int64_t)piece * E * D + (int64_t)e * D + kbeg + 8 * c;
+    if (e0 + rr < E) bmask |= 1u << q;
   }
-  auto issue = [&](int kstep) {
-    char* st = lds + (kstep & 1) * RB_STAGE;
-    const int k0 = kstep * RB_BK;
-    __builtin_amdgcn_global_load_lds((const void*)(srcA + k0), (lds_void*)(st + wave * 1024), 16, 0, 0);
-#pragma unroll
-    for (int q = 0; q < RB_NB; ++q)
-      __builtin_amdgcn_global_load_lds((const void*)(srcB[q] + k0), (lds_void*)(st + RB_A_BYTES + (q * 4 + wave) * 1024),
-                                       16, 0, 0);
-  };
 
   f32x16 acc[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
-  const int sw = rb_swz(lane & 31);
-  const int a_off = (wm * 32 + (lane & 31)) * RB_ROWB;
-
-  if (nk > 0) issue(0);
-  for (int kt = 0; kt < nk; ++kt) {
-    // this wave's loads for step kt are complete; after the barrier everyone's are, and every read of
-    // the stage refilled next (step kt - 1) is done
-    wait_vmcnt<0>();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_barrier();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    if (kt + 1 < nk) issue(kt + 1);
-    const char* st = lds + (kt & 1) * RB_STAGE;
-#pragma unroll
-    for (int kk = 0; kk < RB_BK / 16; ++kk) {
-      const int coff = ((2 * kk + (lane >> 5)) ^ sw) * 16;
-      const bf16x8 af = *(const bf16x8*)(st + a_off + coff);
-#pragma unroll
-      for (int piece = 2; piece >= 0; --piece)  // smallest piece first
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int brow = piece * RB_BN + wn * 64 + j * 32 + (lane & 31);
-          const bf16x8 bf = *(const bf16x8*)(st + RB_A_BYTES + brow * RB_ROWB + coff);
-          acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc[j], 0, 0, 0);
-        }
-    }
-  }
+  const int live = E - (e0 + wn * 64);  // experts inside E from this wave's first column on
+  const int nj = live > 32 ? 2 : live > 0 ? 1 : 0;
+  if (nj == 2)
+    rb_loop<2>(lds, srcA, srcB, bmask, nk, wave, lane, wm, wn, acc);
+  else if (nj == 1)
+    rb_loop<1>(lds, srcA, srcB, bmask, nk, wave, lane, wm, wn, acc);
+  else
+    rb_loop<0>(lds, srcA, srcB, bmask, nk, wave, lane, wm, wn, acc);
   // 32x32 C layout: lane holds column lane % 32, rows 8 (r / 4) + 4 (lane / 32) + r % 4.
   float* out = part + (int64_t)ks * N * E;
 #pragma unroll
