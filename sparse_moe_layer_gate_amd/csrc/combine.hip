@@ -54,17 +54,20 @@ __device__ inline void store8(float* p, const float* acc) {
   *(float4*)(p + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
 }
 
-// One block per token; each thread owns 8 consecutive features per pass.
+// One block per token; each thread owns 8 consecutive features per pass (the launch sizes the block so
+// that a row of up to 8192 features takes one pass).
 template <typename T>
-__global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ Y, const T* __restrict__ Ysh,
+__global__ __launch_bounds__(1024) void combine_kernel(const T* __restrict__ Y, const T* __restrict__ Ysh,
                                                       const int32_t* __restrict__ inv_row, int k, int D,
                                                       float alpha_out, T* __restrict__ y) {
   __shared__ int rows[MAX_K];
   const int64_t n = blockIdx.x;
   if (threadIdx.x < k) rows[threadIdx.x] = inv_row[n * k + threadIdx.x];
   __syncthreads();
-  for (int c = threadIdx.x * 8; c < D; c += 256 * 8) {
+  for (int c = threadIdx.x * 8; c < D; c += blockDim.x * 8) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    V8<T> vsh;
+    if (Ysh) vsh = load8(Ysh + n * D + c);  // in flight with the slot rows
     // slots in groups of 8: the group's row loads are all issued before the first add (a loop of
     // load-then-add waited out one memory latency per slot); the adds keep slot order
     for (int s0 = 0; s0 < k; s0 += 8) {
@@ -80,7 +83,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ Y, c
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = __fmul_rn(acc[i], alpha_out);  // exact when alpha_out == 1
-    if (Ysh) add8(acc, Ysh + n * D + c);
+    if (Ysh) add8(acc, vsh);
     store8(y + n * D + c, acc);
   }
 }
@@ -89,11 +92,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ Y, c
 
 hipError_t launch_combine(int dtype, const void* Y, const void* Ysh, const int32_t* inv_row, int64_t N, int k, int D,
                           float alpha_out, void* y, hipStream_t s) {
+  // one thread per 8 features, whole waves, at most 1024 (D is a multiple of 64)
+  int threads = (D / 8 + 63) / 64 * 64;
+  if (threads > 1024) threads = 1024;
   if (dtype == MOE_F32)
-    hipLaunchKernelGGL(combine_kernel<float>, dim3((unsigned)N), dim3(256), 0, s, (const float*)Y, (const float*)Ysh,
-                       inv_row, k, D, alpha_out, (float*)y);
+    hipLaunchKernelGGL(combine_kernel<float>, dim3((unsigned)N), dim3(threads), 0, s, (const float*)Y,
+                       (const float*)Ysh, inv_row, k, D, alpha_out, (float*)y);
   else
-    hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3((unsigned)N), dim3(256), 0, s, (const uint16_t*)Y,
+    hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3((unsigned)N), dim3(threads), 0, s, (const uint16_t*)Y,
                        (const uint16_t*)Ysh, inv_row, k, D, alpha_out, (uint16_t*)y);
   return hipGetLastError();
 }
