@@ -141,8 +141,8 @@ __global__ __launch_bounds__(512) void scan_kernel(const int32_t* __restrict__ c
 
 // Stable placement of one chunk: rounds of 256 pairs (in pair order); inside a round, a pair's
 // position is its expert's running offset + the pairs of that expert in earlier waves of the round +
-// those in earlier lanes of its own wave (found with 64 shuffles). Tokens stay ascending inside each
-// expert because pairs are visited in (token, slot) order.
+// those in earlier lanes of its own wave (found with one ballot per bit of the expert id). Tokens stay
+// ascending inside each expert because pairs are visited in (token, slot) order.
 __global__ __launch_bounds__(256) void place_kernel(const int32_t* __restrict__ idx, int64_t N, int k, int E,
                                                     const int32_t* __restrict__ chunk_base,
                                                     int32_t* __restrict__ sorted_pair, int32_t* __restrict__ inv_row) {
@@ -151,6 +151,7 @@ __global__ __launch_bounds__(256) void place_kernel(const int32_t* __restrict__ 
   const int c = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int64_t first = (int64_t)c * CH * k;
   const int npairs = (int)(min((int64_t)(c + 1) * CH, N) * k - first);
+  const int ebits = E > 1 ? 32 - __clz(E - 1) : 0;  // bits of the largest expert id
   for (int e = t; e < E; e += 256) {
     running[e] = chunk_base[(int64_t)c * E + e];
     for (int w = 0; w < 4; ++w) wcnt[w][e] = 0;
@@ -166,12 +167,15 @@ __global__ __launch_bounds__(256) void place_kernel(const int32_t* __restrict__ 
         inv_row[first + p] = -1;
       }
     }
-    int rank = 0;
-    for (int j = 0; j < 64; ++j) {
-      const int ej = __shfl(e, j);
-      rank += (j < lane && ej == e) ? 1 : 0;
+    // lanes of this wave holding the same expert: one ballot per bit of the expert id
+    uint64_t same = __ballot(e >= 0);
+    for (int b = 0; b < ebits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t m = __ballot(bit);
+      same &= bit ? m : ~m;
     }
-    if (e >= 0) atomicAdd(&wcnt[wave][e], 1);
+    const int rank = __popcll(same & ((1ull << lane) - 1));  // same-expert lanes before this one
+    if (e >= 0 && rank == 0) wcnt[wave][e] = __popcll(same);
     __syncthreads();
     if (e >= 0) {
       int pos = running[e] + rank;
