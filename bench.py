@@ -162,8 +162,8 @@ def algorithmic_bytes(w: synth.Workload, N: int, distinct: int) -> dict:
 
 
 def is_decode(w: synth.Workload) -> bool:
-    """Batches under 8 rows per expert on average run the weight-streaming kernels."""
-    return w.N * w.k < 8 * w.E
+    """Batches under 4 rows per expert on average run the weight-streaming kernels."""
+    return w.N * w.k < 4 * w.E
 
 
 def measure(w: synth.Workload, r: dict) -> dict:

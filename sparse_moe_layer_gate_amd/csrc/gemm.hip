@@ -139,15 +139,16 @@ int64_t max_tiles(int64_t N, int k, int E, int n_shared_problem, int bm) {
 }
 
 #ifndef MOE_DECODE_ROWS
-#define MOE_DECODE_ROWS 8  // average rows per expert below which the decode kernels run
+#define MOE_DECODE_ROWS 4  // average rows per expert below which the decode kernels run
 #endif
 
 int gemm_bm(int dtype, int64_t N, int k, int E) {
   if (dtype == MOE_F32) return F_BM;
-  // Measured (prefill kernel = the ping-pong kernel): with uniform routing the two kernels tie at ~8
-  // rows per expert and the decode kernel is 4-15% ahead at 6-7; with skewed routing the decode
-  // kernel's 16-row tiles re-stream a hot expert's weights once per 16 rows and lose 28-37% already
-  // at 6-10 rows per expert on average.
+  // Measured (layer ms, decode kernel against the persistent prefill kernel): with uniform routing
+  // (GLM-5 weights) they are within ~3% of each other from 3 to 6 rows per expert and the prefill
+  // kernel leads from 7 on (N = 224: 3.30 -> 3.14); with skewed routing (GLM-4.5 weights) the decode
+  // kernel's 16-row tiles re-stream a hot expert's weights once per 16 rows and lose 30-43% already at
+  // 4.8-6.4 rows per expert (N = 96: 0.61 against 0.47 ms, N = 128: 0.74 against 0.52 ms).
   if (N * k < (int64_t)MOE_DECODE_ROWS * E) return 16;  // weight-streaming decode kernel, 16-row tiles
   return 256;                                           // prefill kernels, 256-row tiles
 }

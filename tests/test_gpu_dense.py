@@ -37,7 +37,7 @@ def _check(w, x, y, tokens, weights):
 
 
 CASES = [
-    dict(N=1, D=256, dff=128), dict(N=5, D=320, dff=192),           # 16-row (decode) tiles
+    dict(N=1, D=256, dff=128), dict(N=3, D=320, dff=192),           # 16-row (decode) tiles
     dict(N=9, D=320, dff=192), dict(N=300, D=256, dff=384),         # 256-row tiles, ragged
     dict(N=1000, D=320, dff=192),
     dict(N=200, D=256, dff=256, limit=10.0, outlier_every=3),       # clamped, outlier tokens

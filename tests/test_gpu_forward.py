@@ -46,11 +46,11 @@ SMALL = [
     dict(N=150, D=320, E=16, G=1, TG=1, k=2, d=192, n_shared=1, alpha=2.5, skew=1.0),
     # the widest routing the ABI takes (E = 512 in 64 groups, k = 32): decode tiles, then 256-row tiles,
     # and a combine over 32 slots
-    dict(N=64, D=128, E=512, G=64, TG=8, k=32, d=64, n_shared=1, alpha=2.5),
+    dict(N=48, D=128, E=512, G=64, TG=8, k=32, d=64, n_shared=1, alpha=2.5),
     dict(N=1024, D=128, E=512, G=64, TG=8, k=32, d=64, n_shared=1, alpha=2.5),
     # 16-row (decode) tiles with column tails and a short last K stage (D = 320, d = 192); the
     # skewed router gives some experts several 16-row tiles
-    dict(N=30, D=320, E=24, G=4, TG=2, k=4, d=192, n_shared=1, alpha=2.5),
+    dict(N=23, D=320, E=24, G=4, TG=2, k=4, d=192, n_shared=1, alpha=2.5),
     dict(N=60, D=320, E=64, G=1, TG=1, k=4, d=192, n_shared=1, alpha=2.5, skew=1.0),
     dict(N=1, D=256, E=16, G=4, TG=2, k=4, d=128, n_shared=1, alpha=2.5),
     dict(N=3, D=128, E=8, G=2, TG=1, k=1, d=64, n_shared=1, alpha=2.5),

@@ -24,7 +24,7 @@ BASE = synth.WORKLOADS["tiny_fp32"]
 
 CLAMP = [
     # 16-row (decode) tiles, a group stage, 2 shared experts
-    dict(N=30, D=256, E=32, G=8, TG=3, k=6, d=128, n_shared=2),
+    dict(N=21, D=256, E=32, G=8, TG=3, k=6, d=128, n_shared=2),
     # 256-row prefill tiles with few rows per expert (150 on average) and column tails
     dict(N=600, D=320, E=16, G=4, TG=2, k=4, d=192, n_shared=1),
     # 256-row prefill tiles
