@@ -504,6 +504,103 @@ __device__ __attribute__((always_inline)) inline void wave8_loop(char* lds, __am
   }
 }
 
+// The K loop of one wave for a tile of at most 64 valid rows. Such a block is a stream of its expert's
+// weights, and its speed is set by how many bytes are in flight, so the 160 KiB are laid out for that:
+// four stages of the tile's 64 A rows (8 KiB each) and four of B (32 KiB each), with three steps of
+// loads in flight where the large-tile ring has two. Every wave issues one A load (its 8 of the 64
+// rows; rows past the tile repeat its last row) and NL B loads per step, so a fixed count of loads
+// per step orders the ring through vmcnt. Waves 0-3 compute 32 rows each (m0 = 0 or 32, MI <= 1).
+template <bool GATE_UP>
+struct SmallRing {
+  static constexpr int S = 4;                                  // stages of A and of B
+  static constexpr int A_STAGE = 64 * Wave8Tile<GATE_UP>::ROWB;  // 8 KiB
+  static constexpr int B_BASE = S * A_STAGE;
+  static_assert(B_BASE + S * Wave8Tile<GATE_UP>::OPB == Wave8Tile<GATE_UP>::RING, "the small ring fills the LDS");
+};
+
+template <bool GATE_UP, int MI>
+__device__ __attribute__((always_inline)) inline void wave8_loop_small(char* lds, __amdgpu_buffer_rsrc_t rsrcA,
+                                                                       uint32_t offA1, __amdgpu_buffer_rsrc_t rsrcB,
+                                                                       const uint32_t (&offB)[4], f32x16 (&acc)[2][4],
+                                                                       int nk, int grp, int q, int wave, int lane,
+                                                                       int m0, int wn) {
+  using T = Wave8Tile<GATE_UP>;
+  using R = SmallRing<GATE_UP>;
+  constexpr int NL = T::NL, TN = 4, ROWB = T::ROWB, S = R::S;
+  constexpr int PER = NL + 1;  // loads per wave and step
+  const int sw = T::swz(lane & 31);
+  const int a_off = (m0 + (lane & 31)) * ROWB;
+  int b_off[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) b_off[j] = (T::b_row(j, wn) + (lane & 31)) * ROWB;
+  bf16x8 af[2][2][MI > 0 ? MI : 1], bfr[2][2][TN];
+  const int half_off = grp * (T::OPB / 2) + q * 1024;
+
+  // step kstep's loads into stage kstep % S: this wave's 8 A rows (chunks [64 wave, + 64)) and its B
+  // chunks as in the large-tile ring
+  auto issue = [&](int kstep) {
+    char* da = lds + (kstep % S) * R::A_STAGE + wave * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrcA, (lds_void*)da, 16, (int)offA1, kstep * T::BK * 2, 0, 0);
+    char* db = lds + R::B_BASE + (kstep % S) * T::OPB + half_off;
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrcB, (lds_void*)(db + i * 4096), 16, (int)offB[i], kstep * T::BK * 2,
+                                               0, 0);
+  };
+  auto read_frags = [&](int kstep, int h) {
+    const char* sa = lds + (kstep % S) * R::A_STAGE;
+    const char* sb = lds + R::B_BASE + (kstep % S) * T::OPB;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int coff = ((2 * (2 * h + s) + (lane >> 5)) ^ sw) * 16;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bfr[h][s][j] = *(const bf16x8*)(sb + b_off[j] + coff);
+#pragma unroll
+      for (int i = 0; i < MI; ++i) af[h][s][i] = *(const bf16x8*)(sa + a_off + i * 32 * ROWB + coff);
+    }
+  };
+  auto compute = [&](int h) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[h][s][i], bfr[h][s][j], acc[i][j], 0, 0, 0);
+  };
+
+  // prologue: steps 0-2; wait for step 0
+  issue(0);
+  if (nk > 1) issue(1);
+  if (nk > 2) issue(2);
+  if (nk > 2)
+    wait_vmcnt<2 * PER>();
+  else if (nk > 1)
+    wait_vmcnt<PER>();
+  else
+    wait_vmcnt<0>();
+  bare_barrier();
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 3 < nk) issue(kt + 3);  // into the stage step kt - 1 used (every wave is done with it)
+    read_frags(kt, 0);
+    wait_lgkm0();
+    read_frags(kt, 1);
+    compute(0);
+    wait_lgkm0();
+    compute(1);
+    // step kt + 1 has landed (steps kt + 2 and kt + 3 may still be in flight)
+    if (kt + 1 < nk) {
+      if (kt + 3 < nk)
+        wait_vmcnt<2 * PER>();
+      else if (kt + 2 < nk)
+        wait_vmcnt<PER>();
+      else
+        wait_vmcnt<0>();
+    }
+    bare_barrier();
+  }
+}
+
 // One logical block of the eight-wave kernel: row tile and column tile from the logical id L, K loop,
 // epilogue. Every wave of the block calls it with the same arguments.
 template <bool GATE_UP>
@@ -528,7 +625,11 @@ __device__ __forceinline__ void w8_block(const GroupedArgs& a, int ncol_max, int
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int grp = wave >> 2, q = wave & 3;
-  const int m0 = grp * 128 + (q & 1) * 64, wn = q >> 1;
+  // gate_up tiles of at most 64 rows run the weight-streaming ring (wave8_loop_small): waves 0-3
+  // compute 32 rows each; otherwise each wave computes 64 of the 256 rows. (The down GEMM's short K
+  // loop did not gain from it: 1.37 -> 1.41 ms on the skewed GLM-4.5 layer.)
+  const bool small = GATE_UP && tile.rows <= 64;
+  const int m0 = small && grp == 0 ? (q & 1) * 32 : grp * 128 + (q & 1) * 64, wn = q >> 1;
 
   // Direct-load sources: chunk p of this half's 128 rows is row 128 g + p / 8, slot p % 8, which holds
   // the row's logical chunk slot ^ swz(row). Both operands are read through raw buffer descriptors
@@ -555,6 +656,14 @@ __device__ __forceinline__ void w8_block(const GroupedArgs& a, int ncol_max, int
       offA[i] = kNoRow;  // past the tile's valid rows: not loaded
     }
   }
+  // small ring: this lane's A chunk is row 8 wave + lane / 8 (past the tile: its last row), slot lane % 8
+  uint32_t offA1 = 0;
+  if (small) {
+    const int r = 8 * wave + (lane >> 3), c = (lane & 7) ^ T::swz(r);
+    const int rr = min(r, tile.rows - 1);
+    const int64_t g = P.gather ? a.sorted_pair[(int64_t)tile.row_start + rr] / a.k : rr;
+    offA1 = (uint32_t)(g * P.lda + 8 * c) * 2;
+  }
   // down: this thread's row scale, read now so its latency hides under the K loop
   float wscale = 1.0f;
   if (!GATE_UP && t < 256 && P.scale_rows) wscale = a.topk_w[a.sorted_pair[tile.row_start + min(t, tile.rows - 1)]];
@@ -569,13 +678,19 @@ __device__ __forceinline__ void w8_block(const GroupedArgs& a, int ncol_max, int
 
   const int nk = P.K / T::BK;
   const int live_m = tile.rows - m0;
-  const int mi = live_m <= 0 ? 0 : min(2, (live_m + 31) / 32);
-  if (mi == 2)
+  const int mi = live_m <= 0 || (small && grp == 1) ? 0 : min(small ? 1 : 2, (live_m + 31) / 32);
+  if (small) {
+    if (mi == 1)
+      wave8_loop_small<GATE_UP, 1>(lds, rsrcA, offA1, rsrcB, offB, acc, nk, grp, q, wave, lane, m0, wn);
+    else
+      wave8_loop_small<GATE_UP, 0>(lds, rsrcA, offA1, rsrcB, offB, acc, nk, grp, q, wave, lane, m0, wn);
+  } else if (mi == 2) {
     wave8_loop<GATE_UP, 2>(lds, rsrcA, offA, rsrcB, offB, acc, nk, grp, q, lane, m0, wn);
-  else if (mi == 1)
+  } else if (mi == 1) {
     wave8_loop<GATE_UP, 1>(lds, rsrcA, offA, rsrcB, offB, acc, nk, grp, q, lane, m0, wn);
-  else
+  } else {
     wave8_loop<GATE_UP, 0>(lds, rsrcA, offA, rsrcB, offB, acc, nk, grp, q, lane, m0, wn);
+  }
 
   // Epilogue through LDS (the loop ended on a barrier after the last operand read): each wave stages
   // its 64 x OC bf16 results (SwiGLU / weight scale applied) in its own padded region, then stores
@@ -607,7 +722,7 @@ __device__ __forceinline__ void w8_block(const GroupedArgs& a, int ncol_max, int
   uint16_t* out = (uint16_t*)P.out;
   const int ocol0 = col0 + wn * OC;
   constexpr int CH = OC / 8;  // 16-byte chunks per staged row
-  const int rows_here = min(64, tile.rows - m0);
+  const int rows_here = min(32 * mi, tile.rows - m0);  // the rows this wave computed and staged
   for (int c = lane; c < rows_here * CH; c += 64) {
     const int row = c / CH, ch = c % CH;
     const int col = ocol0 + ch * 8;
