@@ -139,25 +139,27 @@ __global__ __launch_bounds__(512) void scan_kernel(const int32_t* __restrict__ c
   build_tiles(t1, e < E, e, cnt, off, N, n_shared_problem, wsum);
 }
 
-// Stable placement of one chunk: rounds of 256 pairs (in pair order); inside a round, a pair's
+// Stable placement of one chunk: rounds of PL pairs (in pair order); inside a round, a pair's
 // position is its expert's running offset + the pairs of that expert in earlier waves of the round +
 // those in earlier lanes of its own wave (found with one ballot per bit of the expert id). Tokens stay
 // ascending inside each expert because pairs are visited in (token, slot) order.
-__global__ __launch_bounds__(256) void place_kernel(const int32_t* __restrict__ idx, int64_t N, int k, int E,
+constexpr int PL = 512, PW = PL / 64;  // threads (pairs per round) and waves of a placement block
+
+__global__ __launch_bounds__(PL) void place_kernel(const int32_t* __restrict__ idx, int64_t N, int k, int E,
                                                     const int32_t* __restrict__ chunk_base,
                                                     int32_t* __restrict__ sorted_pair, int32_t* __restrict__ inv_row) {
   __shared__ int running[MAX_E];
-  __shared__ int wcnt[4][MAX_E];
+  __shared__ int wcnt[PW][MAX_E];
   const int c = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int64_t first = (int64_t)c * CH * k;
   const int npairs = (int)(min((int64_t)(c + 1) * CH, N) * k - first);
   const int ebits = E > 1 ? 32 - __clz(E - 1) : 0;  // bits of the largest expert id
-  for (int e = t; e < E; e += 256) {
+  for (int e = t; e < E; e += PL) {
     running[e] = chunk_base[(int64_t)c * E + e];
-    for (int w = 0; w < 4; ++w) wcnt[w][e] = 0;
+    for (int w = 0; w < PW; ++w) wcnt[w][e] = 0;
   }
   __syncthreads();
-  for (int r0 = 0; r0 < npairs; r0 += 256) {
+  for (int r0 = 0; r0 < npairs; r0 += PL) {
     const int p = r0 + t;
     int e = -1;
     if (p < npairs) {
@@ -184,9 +186,13 @@ __global__ __launch_bounds__(256) void place_kernel(const int32_t* __restrict__ 
       inv_row[first + p] = pos;
     }
     __syncthreads();
-    for (int e2 = t; e2 < E; e2 += 256) {
-      running[e2] += wcnt[0][e2] + wcnt[1][e2] + wcnt[2][e2] + wcnt[3][e2];
-      for (int w = 0; w < 4; ++w) wcnt[w][e2] = 0;
+    for (int e2 = t; e2 < E; e2 += PL) {
+      int add = 0;
+      for (int w = 0; w < PW; ++w) {
+        add += wcnt[w][e2];
+        wcnt[w][e2] = 0;
+      }
+      running[e2] += add;
     }
     __syncthreads();
   }
@@ -247,7 +253,7 @@ hipError_t launch_scan(const int32_t* chunk_counts, int nchunks, int64_t N, int 
 hipError_t launch_place(const int32_t* idx, int64_t N, int k, int E, const int32_t* chunk_base, int32_t* sorted_pair,
                         int32_t* inv_row, hipStream_t s) {
   const int nchunks = (int)((N + CH - 1) / CH);
-  hipLaunchKernelGGL(place_kernel, dim3(nchunks), dim3(256), 0, s, idx, N, k, E, chunk_base, sorted_pair, inv_row);
+  hipLaunchKernelGGL(place_kernel, dim3(nchunks), dim3(PL), 0, s, idx, N, k, E, chunk_base, sorted_pair, inv_row);
   return hipGetLastError();
 }
 
