@@ -46,47 +46,114 @@ __global__ __launch_bounds__(256) void split_kernel(const float* __restrict__ wg
 
 // ---------------------------------------------------------------------------------------------
 // bf16 gate GEMM: part[ks, n, e] = sum over the ks-th hidden range of x[n, t] (lo + mid + hi)[e, t].
-// Block tile 64 tokens x 128 experts, K step 32, two-stage LDS ring fed by global_load_lds_dwordx4
-// (the swizzled chunk layout of the expert GEMMs); 4 waves in 2 x 2, each 32 tokens x 64 experts
-// as 1 x 2 tiles of v_mfma_f32_32x32x16_bf16 per piece.
-constexpr int RB_BM = 64, RB_BN = 128, RB_BK = 32, RB_ROWB = RB_BK * 2, RB_CPR = 4;
-constexpr int RB_A_BYTES = RB_BM * RB_ROWB, RB_B_BYTES = 3 * RB_BN * RB_ROWB;
-constexpr int RB_STAGE = RB_A_BYTES + RB_B_BYTES;
-constexpr int RB_NB = 3 * RB_BN * RB_CPR / 256;  // B loads per thread per K step (A: 1)
+// A block covers 128 tokens and NJ 32-expert column tiles (all of E up to 256, so x is read once per
+// K range), K step 32, an S-stage LDS ring fed by global_load_lds_dwordx4 (the swizzled chunk layout of
+// the expert GEMMs); each of the 4 waves owns 32 tokens x all NJ column tiles, v_mfma_f32_32x32x16_bf16
+// per piece. The gate GEMM is small and wait-bound, so the ring is as deep as the LDS allows (S - 1
+// steps of loads in flight).
+constexpr int RB_BM = 128, RB_BK = 32, RB_ROWB = RB_BK * 2, RB_CPR = 4;
+constexpr int RB_A_BYTES = RB_BM * RB_ROWB;                // 8 KiB
+constexpr int RB_A_LOADS = RB_BM * RB_CPR / 256;            // A loads per thread per K step
+
+template <int NJ>
+struct RouterTile {
+  static constexpr int BN = 32 * NJ;                             // experts per block
+  static constexpr int B_CHUNKS = 3 * BN * RB_CPR;               // 16-byte chunks of the three pieces
+  static constexpr int B_LOADS = (B_CHUNKS + 255) / 256;         // B loads per thread per K step
+  static constexpr int STAGE = RB_A_BYTES + B_LOADS * 256 * 16;  // the last load's spare chunks land at the end
+  static constexpr int S = (160 * 1024) / STAGE < 4 ? (160 * 1024) / STAGE : 4;
+  static constexpr int LOADS = RB_A_LOADS + B_LOADS;             // loads per thread per K step
+  static_assert(S >= 2, "two stages at least");
+  static_assert((S - 2) * LOADS < 64, "vmcnt is 6 bits");
+};
 
 __device__ inline int rb_swz(int r) {
   r &= 31;
   return ((r >> 1) ^ (r >> 3)) & 3;
 }
 
-// The K loop of one wave with NJ of its two 32-expert column tiles inside E (column tiles past E, as in
-// the last block column when E is not a multiple of 128, issue no MFMAs). Every wave runs the same
-// loads and barriers whatever its NJ.
+// Blocks are numbered (K range, column block)-major, token block minor, and dealt to the XCDs in
+// contiguous runs (xcd_logical_block), so an XCD works through few K ranges of the weight pieces and
+// they stay in its L2 while its token blocks stream x.
 template <int NJ>
-__device__ __forceinline__ void rb_loop(char* lds, const uint16_t* srcA, const uint16_t* const (&srcB)[RB_NB],
-                                        uint32_t bmask, int nk, int wave, int lane, int wm, int wn, f32x16 (&acc)[2]) {
-  auto issue = [&](int kstep) {
-    char* st = lds + (kstep & 1) * RB_STAGE;
-    const int k0 = kstep * RB_BK;
-    __builtin_amdgcn_global_load_lds((const void*)(srcA + k0), (lds_void*)(st + wave * 1024), 16, 0, 0);
+__global__ __launch_bounds__(256) void logits_bf16x3_kernel(const uint16_t* __restrict__ x,
+                                                            const uint16_t* __restrict__ w3, int64_t N, int D, int E,
+                                                            int kchunk, int ks_count, float* __restrict__ part) {
+  using T = RouterTile<NJ>;
+  constexpr int S = T::S;
+  __shared__ __attribute__((aligned(1024))) char lds[S * T::STAGE];
+  const int64_t row_blocks = (N + RB_BM - 1) / RB_BM;
+  const int col_blocks = (E + T::BN - 1) / T::BN;
+  const int64_t L = xcd_logical_block(row_blocks * col_blocks * ks_count);
+  if (L < 0) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t n0 = (L % row_blocks) * RB_BM;
+  const int64_t slice = L / row_blocks;
+  const int e0 = (int)(slice % col_blocks) * T::BN;
+  const int ks = (int)(slice / col_blocks);
+  const int kbeg = ks * kchunk;
+  const int nk = min(kchunk, D - kbeg) / RB_BK;
+
+  // direct-load sources (fixed rows; the K offset advances): load q of this thread fills chunk
+  // p = (4 q + wave) 64 + lane of its operand, i.e. row p / 4, slot p % 4 holding the row's logical
+  // chunk slot ^ swz(row). Every lane loads: B chunks past the three pieces repeat the last one (into
+  // spare space at the end of the stage), experts past E repeat expert E - 1 (never stored).
+  const uint16_t* srcA[RB_A_LOADS];
 #pragma unroll
-    for (int q = 0; q < RB_NB; ++q)
-      if (bmask & (1u << q))  // rows of experts past E are not loaded (nothing reads them)
-        __builtin_amdgcn_global_load_lds((const void*)(srcB[q] + k0),
-                                         (lds_void*)(st + RB_A_BYTES + (q * 4 + wave) * 1024), 16, 0, 0);
+  for (int q = 0; q < RB_A_LOADS; ++q) {
+    const int p = (q * 4 + wave) * 64 + lane, r = p / RB_CPR, c = (p % RB_CPR) ^ rb_swz(r);
+    const int64_t n = min(n0 + r, N - 1);
+    srcA[q] = x + n * D + kbeg + 8 * c;
+  }
+  const uint16_t* srcB[T::B_LOADS];
+#pragma unroll
+  for (int q = 0; q < T::B_LOADS; ++q) {
+    const int p = min((q * 4 + wave) * 64 + lane, T::B_CHUNKS - 1);
+    const int piece = p / (T::BN * RB_CPR), rr = (p % (T::BN * RB_CPR)) / RB_CPR;
+    const int c = (p % RB_CPR) ^ rb_swz(rr);
+    const int e = min(e0 + rr, E - 1);
+    srcB[q] = w3 + (int64_t)piece * E * D + (int64_t)e * D + kbeg + 8 * c;
+  }
+  auto issue = [&](int kstep) {
+    char* st = lds + (kstep % S) * T::STAGE;
+    const int k0 = kstep * RB_BK;
+#pragma unroll
+    for (int q = 0; q < RB_A_LOADS; ++q)
+      __builtin_amdgcn_global_load_lds((const void*)(srcA[q] + k0), (lds_void*)(st + (q * 4 + wave) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int q = 0; q < T::B_LOADS; ++q)
+      __builtin_amdgcn_global_load_lds((const void*)(srcB[q] + k0),
+                                       (lds_void*)(st + RB_A_BYTES + (q * 4 + wave) * 1024), 16, 0, 0);
   };
+
+  f32x16 acc[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
   const int sw = rb_swz(lane & 31);
-  const int a_off = (wm * 32 + (lane & 31)) * RB_ROWB;
-  if (nk > 0) issue(0);
+  const int a_off = (wave * 32 + (lane & 31)) * RB_ROWB;
+
+#pragma unroll
+  for (int t = 0; t < S - 1; ++t)
+    if (t < nk) issue(t);
   for (int kt = 0; kt < nk; ++kt) {
-    // this wave's loads for step kt are complete; after the barrier everyone's are, and every read of
-    // the stage refilled next (step kt - 1) is done
-    wait_vmcnt<0>();
+    // step kt's loads are complete (later steps' may be in flight; every thread issues T::LOADS per
+    // step); after the barrier everyone's are, and every read of the stage refilled next (step kt - 1)
+    // is done
+    const int ahead = min(S - 2, nk - 1 - kt);  // steps issued after kt
+    if (S > 3 && ahead >= 2) {
+      wait_vmcnt<(S > 3 ? 2 : 0) * T::LOADS>();
+    } else if (S > 2 && ahead >= 1) {
+      wait_vmcnt<(S > 2 ? 1 : 0) * T::LOADS>();
+    } else {
+      wait_vmcnt<0>();
+    }
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_barrier();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    if (kt + 1 < nk) issue(kt + 1);
-    const char* st = lds + (kt & 1) * RB_STAGE;
+    if (kt + S - 1 < nk) issue(kt + S - 1);
+    const char* st = lds + (kt % S) * T::STAGE;
 #pragma unroll
     for (int kk = 0; kk < RB_BK / 16; ++kk) {
       const int coff = ((2 * kk + (lane >> 5)) ^ sw) * 16;
@@ -95,68 +162,31 @@ __device__ __forceinline__ void rb_loop(char* lds, const uint16_t* srcA, const u
       for (int piece = 2; piece >= 0; --piece)  // smallest piece first
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-          const int brow = piece * RB_BN + wn * 64 + j * 32 + (lane & 31);
+          const int brow = piece * T::BN + j * 32 + (lane & 31);
           const bf16x8 bf = *(const bf16x8*)(st + RB_A_BYTES + brow * RB_ROWB + coff);
           acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc[j], 0, 0, 0);
         }
     }
   }
-}
-
-__global__ __launch_bounds__(256) void logits_bf16x3_kernel(const uint16_t* __restrict__ x,
-                                                            const uint16_t* __restrict__ w3, int64_t N, int D, int E,
-                                                            int kchunk, float* __restrict__ part) {
-  __shared__ __attribute__((aligned(1024))) char lds[2 * RB_STAGE];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
-  const int64_t n0 = (int64_t)blockIdx.x * RB_BM;
-  const int e0 = blockIdx.y * RB_BN;
-  const int ks = blockIdx.z;
-  const int kbeg = ks * kchunk;
-  const int nk = min(kchunk, D - kbeg) / RB_BK;
-
-  // direct-load sources (fixed rows; the K offset advances)
-  const uint16_t* srcA;
-  {
-    const int p = wave * 64 + lane, r = p / RB_CPR, c = (p % RB_CPR) ^ rb_swz(r);
-    const int64_t n = min(n0 + r, N - 1);
-    srcA = x + n * D + kbeg + 8 * c;
-  }
-  const uint16_t* srcB[RB_NB];
-  uint32_t bmask = 0;
-#pragma unroll
-  for (int q = 0; q < RB_NB; ++q) {
-    const int p = (q * 4 + wave) * 64 + lane;
-    const int piece = p / (RB_BN * RB_CPR), rr = (p % (RB_BN * RB_CPR)) / RB_CPR;
-    const int c = (p % RB_CPR) ^ rb_swz(rr);
-    const int e = min(e0 + rr, E - 1);
-    srcB[q] = w3 + (int64_t)piece * E * D + (int64_t)e * D + kbeg + 8 * c;
-    if (e0 + rr < E) bmask |= 1u << q;
-  }
-
-  f32x16 acc[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
-  const int live = E - (e0 + wn * 64);  // experts inside E from this wave's first column on
-  const int nj = live > 32 ? 2 : live > 0 ? 1 : 0;
-  if (nj == 2)
-    rb_loop<2>(lds, srcA, srcB, bmask, nk, wave, lane, wm, wn, acc);
-  else if (nj == 1)
-    rb_loop<1>(lds, srcA, srcB, bmask, nk, wave, lane, wm, wn, acc);
-  else
-    rb_loop<0>(lds, srcA, srcB, bmask, nk, wave, lane, wm, wn, acc);
   // 32x32 C layout: lane holds column lane % 32, rows 8 (r / 4) + 4 (lane / 32) + r % 4.
   float* out = part + (int64_t)ks * N * E;
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < NJ; ++j)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int64_t n = n0 + wm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      const int e = e0 + wn * 64 + j * 32 + (lane & 31);
+      const int64_t n = n0 + wave * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      const int e = e0 + j * 32 + (lane & 31);
       if (n < N && e < E) out[n * E + e] = acc[j][r];
     }
+}
+
+// Column tiles per block: all of E's 32-expert tiles when there are at most 8, else an even split
+// into blocks of at most 8; at most 2 for batches of one or two token blocks (more blocks to spread
+// over the CUs, shallower per-block work).
+int router_nj(int64_t N, int E) {
+  const int most = (N + RB_BM - 1) / RB_BM <= 2 ? 2 : 8;
+  const int tiles = (E + 31) / 32, blocks = (tiles + most - 1) / most;
+  return (tiles + blocks - 1) / blocks;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -393,10 +423,11 @@ __global__ __launch_bounds__(256) void select_kernel(float* __restrict__ scores,
 RouterPlan router_plan(int dtype, int64_t N, int D, int E) {
   RouterPlan p;
   p.split = dtype == MOE_BF16;
-  const int64_t bm = p.split ? RB_BM : LG_BM, bn = p.split ? RB_BN : LG_BN;
+  const int64_t bm = p.split ? RB_BM : LG_BM, bn = p.split ? 32 * router_nj(N, E) : LG_BN;
   int64_t tiles = ((N + bm - 1) / bm) * ((E + bn - 1) / bn);
   if (tiles < 1) tiles = 1;  // N = 0
-  const int64_t want = (512 + tiles - 1) / tiles;  // aim for 512+ blocks
+  // aim for 256+ blocks (the bf16 kernel's ring takes most of a CU's LDS), 512+ for the float32 kernel
+  const int64_t want = ((p.split ? 256 : 512) + tiles - 1) / tiles;
   int64_t most = D / 256 > 0 ? D / 256 : 1;        // at least 256 of the hidden dimension per split
   if (most > 16) most = 16;                         // and at most 16 partials to add per logit
   const int64_t ks = want < 1 ? 1 : (want > most ? most : want);
@@ -416,8 +447,22 @@ hipError_t launch_router_split(const float* wg, int E, int D, uint16_t* w3, hipS
 hipError_t launch_logits(int dtype, const RouterPlan& p, const void* x, const float* wg, const uint16_t* w3, int64_t N,
                          int D, int E, float* part, hipStream_t s) {
   if (p.split) {
-    dim3 grid((unsigned)((N + RB_BM - 1) / RB_BM), (unsigned)((E + RB_BN - 1) / RB_BN), (unsigned)p.ks);
-    hipLaunchKernelGGL(logits_bf16x3_kernel, grid, dim3(256), 0, s, (const uint16_t*)x, w3, N, D, E, p.kchunk, part);
+    const int nj = router_nj(N, E);
+    const int64_t blocks = (N + RB_BM - 1) / RB_BM * ((E + 32 * nj - 1) / (32 * nj)) * p.ks;
+    dim3 grid((unsigned)((blocks + 7) / 8 * 8));
+    auto go = [&](auto kernel) {
+      hipLaunchKernelGGL(kernel, grid, dim3(256), 0, s, (const uint16_t*)x, w3, N, D, E, p.kchunk, p.ks, part);
+    };
+    switch (nj) {
+      case 1: go(logits_bf16x3_kernel<1>); break;
+      case 2: go(logits_bf16x3_kernel<2>); break;
+      case 3: go(logits_bf16x3_kernel<3>); break;
+      case 4: go(logits_bf16x3_kernel<4>); break;
+      case 5: go(logits_bf16x3_kernel<5>); break;
+      case 6: go(logits_bf16x3_kernel<6>); break;
+      case 7: go(logits_bf16x3_kernel<7>); break;
+      default: go(logits_bf16x3_kernel<8>); break;
+    }
   } else {
     dim3 grid((unsigned)((N + LG_BM - 1) / LG_BM), (unsigned)((E + LG_BN - 1) / LG_BN), (unsigned)p.ks);
     if (dtype == MOE_F32)
