@@ -18,6 +18,8 @@
 //  - blocks follow an XCD-aware order over the valid tiles with a row-tile-major rasterization.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -793,15 +795,16 @@ bool wave8_fits(const GroupedArgs& a) {
 // Blocks of the persistent kernel: one per CU of the current device (a multiple of 8: every XCD gets
 // the same number), queried once per device.
 int64_t persistent_grid() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];  // 0 until queried; callers on several threads may race to fill it
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8) n = 256;
-    cached[dev] = n / 8 * 8;
+    n = n / 8 * 8;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 template <bool GATE_UP>
