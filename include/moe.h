@@ -24,7 +24,8 @@
  *  - Buffers: all tensor pointers are device pointers (HBM), row-major and
  *    contiguous, 16-byte aligned, owned by the caller. The library allocates
  *    nothing and frees nothing on these calls; scratch space is the caller's
- *    `workspace` of at least moe_workspace_size() bytes.
+ *    `workspace` of at least moe_workspace_size() bytes. Calls that may run at
+ *    the same time (on different streams) need separate workspaces.
  *  - Streams: `stream` is a hipStream_t (NULL = the null stream). Every call
  *    enqueues its kernels on it and returns without synchronising.
  *  - Errors: configuration and argument errors are detected on the host before

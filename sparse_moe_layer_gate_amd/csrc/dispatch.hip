@@ -54,14 +54,16 @@ __device__ int block_exclusive_scan(int v, int* wsum, int* total) {
   return before + incl - v;
 }
 
-// Position in the merged list of the i-th small-expert tile (a) and of the j-th other tile (b), with na
-// and nb tiles in the two classes. The merge orders a tile by its fractional rank ((2 i + 1) / (2 na)
-// or (2 j + 1) / (2 nb); a before b on equal ranks), so every stretch of the list holds the two classes
-// in the same proportion.
 // Quotient of p / q for q > 0, in 32 bits when p fits (a 64-bit division is a long emulated sequence).
 __device__ inline uint64_t udiv(uint64_t p, uint32_t q) {
   return p <= 0xffffffffull ? (uint64_t)((uint32_t)p / q) : p / q;
 }
+
+// Position in the merged list of the i-th small-expert tile (a) and of the j-th other tile (b), with na
+// and nb tiles in the two classes. The merge orders a tile by its fractional rank ((2 i + 1) / (2 na)
+// or (2 j + 1) / (2 nb); a before b on equal ranks), so every stretch of the list holds the two classes
+// in the same proportion. (a: the b tiles of smaller rank number ceil((2 i + 1) nb / na) / 2, rounded
+// down; b: the a tiles of rank at most its own number (floor((2 j + 1) na / nb) + 1) / 2.)
 __device__ inline int merged_pos_a(int i, int na, int nb) {
   const uint64_t c = udiv((uint64_t)(2 * i + 1) * nb + na - 1, na);  // ceil
   return i + (int)min((uint64_t)nb, c / 2);
