@@ -420,6 +420,10 @@ __global__ __launch_bounds__(256) void select_kernel(float* __restrict__ scores,
 
 }  // namespace
 
+#ifndef MOE_ROUTER_BLOCKS
+#define MOE_ROUTER_BLOCKS 256  // blocks the bf16 gate GEMM aims for (the K range splits until then)
+#endif
+
 RouterPlan router_plan(int dtype, int64_t N, int D, int E) {
   RouterPlan p;
   p.split = dtype == MOE_BF16;
@@ -427,7 +431,7 @@ RouterPlan router_plan(int dtype, int64_t N, int D, int E) {
   int64_t tiles = ((N + bm - 1) / bm) * ((E + bn - 1) / bn);
   if (tiles < 1) tiles = 1;  // N = 0
   // aim for 256+ blocks (the bf16 kernel's ring takes most of a CU's LDS), 512+ for the float32 kernel
-  const int64_t want = ((p.split ? 256 : 512) + tiles - 1) / tiles;
+  const int64_t want = ((p.split ? MOE_ROUTER_BLOCKS : 512) + tiles - 1) / tiles;
   int64_t most = D / 256 > 0 ? D / 256 : 1;        // at least 256 of the hidden dimension per split
   if (most > 16) most = 16;                         // and at most 16 partials to add per logit
   const int64_t ks = want < 1 ? 1 : (want > most ? most : want);
