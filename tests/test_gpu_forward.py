@@ -94,3 +94,27 @@ def test_device_generator_matches_host():
     assert np.array_equal(H.to_host(dev["sh_gate"]), sg)
     assert np.array_equal(H.to_host(dev["sh_up"]), su)
     assert np.array_equal(H.to_host(dev["sh_down"]), sd)
+
+
+def test_forward_reuses_workspace():
+    """One workspace, sized for the largest batch, serves calls of falling and rising N (256-row tiles,
+    then 16-row tiles, then 256-row tiles again): every output equals that of a call with a fresh
+    workspace, bit for bit. Each call rebuilds the tile lists and zeroes the prefill kernels' work
+    counters, whatever the workspace held."""
+    import torch
+
+    import sparse_moe_layer_gate_amd as moe
+
+    w = replace(synth.WORKLOADS["tiny_fp32"], name="reuse", N=1500, D=256, E=16, G=4, TG=2, k=4, d=128,
+                n_shared=1, alpha=2.5, dtype="bf16", seed=11, skew=1.0)
+    _, _, dev = H.device_weights(w, generate_on_device=False)
+    x_dev = H.to_device(synth.x_host(w))
+    cfg = moe.config_of(w)
+    ws = moe.alloc_workspace(cfg, w.N)
+    for n in (1500, 700, 10, 1500):  # 10 tokens: 40 pairs on 16 experts run the 16-row tiles
+        print(f"[reuse] N={n}", flush=True)
+        y = torch.empty((n, w.D), dtype=x_dev.dtype, device="cuda")
+        moe.moe_forward(cfg, n, x_dev[:n], dev, y, ws)
+        torch.cuda.synchronize()
+        y_fresh, _, _, _ = H.gpu_forward(w, x_dev[:n], dev)
+        assert np.array_equal(H.to_host(y), y_fresh), n
