@@ -101,6 +101,34 @@ def test_scores_within_bound(name):
     assert np.all(margin[differ] <= 2 * tol.max(axis=1)[differ])
 
 
+# Router GEMM tile shapes: E past 256 and not a multiple of 32 (two blocks of five 32-expert tiles, the
+# last partly past E), E = 100 (four tiles, the last partly past E), batches of one token block and of
+# one partial block (two tiles per block), token counts that leave a partial 128-token block.
+GEMM_SHAPES = [
+    dict(N=777, D=256, E=300, k=8),
+    dict(N=260, D=512, E=100, k=6),
+    dict(N=5, D=320, E=40, k=4),
+    dict(N=128, D=192, E=96, k=2),
+]
+
+
+@pytest.mark.parametrize("case", GEMM_SHAPES, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_scores_within_bound_gemm_shapes(case):
+    w = replace(synth.WORKLOADS["tiny_fp32"], name="router_shape", G=1, TG=1, dtype="bf16", seed=13, **case)
+    print(f"[scores] {case}", flush=True)
+    x = synth.x_host(w)
+    wg, b = synth.router_host(w)
+    s_ref = oracle.scores(w, x, wg)
+    s, idx, wt = _route_gpu(w, w.N, x_host=x, wg=wg, b=b)
+    tol = H.score_tolerance(w, x, wg)
+    err = np.abs(s.astype(np.float64) - s_ref)
+    assert np.all(err <= tol), f"max err {err.max():.3g}, worst ratio {(err / tol).max():.3g}"
+    idx_ref, _ = oracle.select(w, s_ref, b)
+    margin = oracle.select_margin(w, s_ref, b)
+    differ = np.any(idx != idx_ref, axis=1)
+    assert np.all(margin[differ] <= 2 * tol.max(axis=1)[differ])
+
+
 def _dispatch_gpu(w, idx):
     import torch
 
