@@ -42,6 +42,9 @@ SMALL = [
     dict(N=77, D=256, E=32, G=8, TG=3, k=6, d=128, n_shared=2, alpha=2.5),
     dict(N=129, D=192, E=12, G=1, TG=1, k=3, d=64, n_shared=0, alpha=2.5),
     dict(N=50, D=256, E=16, G=4, TG=2, k=4, d=128, n_shared=1, alpha=2.5, norm=False),
+    # gate_up tiles of at most 64 rows (the weight-streaming ring) with one- and two-step K loops
+    dict(N=100, D=64, E=8, G=1, TG=1, k=2, d=128, n_shared=1, alpha=2.5),
+    dict(N=100, D=128, E=8, G=2, TG=1, k=2, d=64, n_shared=0, alpha=2.5),
     # 256-row tiles holding few rows (~19 per expert), skewed: some experts span two tiles
     dict(N=150, D=320, E=16, G=1, TG=1, k=2, d=192, n_shared=1, alpha=2.5, skew=1.0),
     # the widest routing the ABI takes (E = 512 in 64 groups, k = 32): decode tiles, then 256-row tiles,
