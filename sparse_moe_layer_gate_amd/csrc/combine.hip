@@ -23,7 +23,11 @@ template <>
 struct V8<float> {
   float4 a, b;
 };
-__device__ inline V8<uint16_t> load8(const uint16_t* p) { return V8<uint16_t>{*(const uint4*)p}; }
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ inline V8<uint16_t> load8(const uint16_t* p) {
+  const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);  // each expert row is read once
+  return V8<uint16_t>{make_uint4(v.x, v.y, v.z, v.w)};
+}
 __device__ inline V8<float> load8(const float* p) { return V8<float>{*(const float4*)p, *(const float4*)(p + 4)}; }
 __device__ inline void add8(float* acc, const V8<uint16_t>& x) {
   const uint32_t w[4] = {x.v.x, x.v.y, x.v.z, x.v.w};
@@ -47,7 +51,8 @@ __device__ inline void store8(uint16_t* p, const float* acc) {
   v.y = (uint32_t)bf16_rne(acc[2]) | ((uint32_t)bf16_rne(acc[3]) << 16);
   v.z = (uint32_t)bf16_rne(acc[4]) | ((uint32_t)bf16_rne(acc[5]) << 16);
   v.w = (uint32_t)bf16_rne(acc[6]) | ((uint32_t)bf16_rne(acc[7]) << 16);
-  *(uint4*)p = v;
+  const u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, (u32x4*)p);
 }
 __device__ inline void store8(float* p, const float* acc) {
   *(float4*)p = make_float4(acc[0], acc[1], acc[2], acc[3]);
