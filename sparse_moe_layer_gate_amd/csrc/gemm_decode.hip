@@ -31,6 +31,13 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 #ifndef MOE_DC_NT
 #define MOE_DC_NT 2
 #endif
+// Cache policy of the weight loads: non-temporal (the NT bit, 2 on gfx950). Each weight byte is read
+// once per launch, and the hint keeps the stream from allocating in the caches: GLM-5 decode gate_up
+// 1.28-1.33 -> 1.17 ms (6.6 TB/s), down 0.62 -> 0.57 ms; the activation rows, re-read by every wave
+// of a tile, keep the default policy.
+#ifndef MOE_DC_WEIGHT_CPOL
+#define MOE_DC_WEIGHT_CPOL 2
+#endif
 
 template <bool GATE_UP>
 struct DecodeTile {
@@ -116,10 +123,11 @@ __global__ __launch_bounds__(256) void grouped_bf16_decode(GroupedArgs a, int nc
 #pragma unroll
     for (int q = 0; q < QPT; ++q) {
       const int64_t ke = (int64_t)t * SK + 8 * min(chunk[q], kmax / 8 - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(src[0][q] + ke), (lds_void*)(st + q * 1024), 16, 0, 0);
 #pragma unroll
-      for (int j = 0; j <= NT; ++j)
+      for (int j = 1; j <= NT; ++j)
         __builtin_amdgcn_global_load_lds((const void*)(src[j][q] + ke), (lds_void*)(st + j * T::TILE_BYTES + q * 1024),
-                                         16, 0, 0);
+                                         16, 0, MOE_DC_WEIGHT_CPOL);
     }
   };
 
