@@ -105,8 +105,11 @@ __device__ void build_tiles(const TileSpec& ts, bool valid, int e, int cnt, int 
 __global__ __launch_bounds__(512) void scan_kernel(const int32_t* __restrict__ chunk_counts, int nchunks, int64_t N,
                                                    int k, int E, int n_shared_problem, int32_t* __restrict__ counts,
                                                    int32_t* __restrict__ offsets, int32_t* __restrict__ chunk_base,
-                                                   TileSpec t0, TileSpec t1) {
+                                                   TileSpec t0, TileSpec t1, int pick_rows) {
   __shared__ int wsum[8];
+  __shared__ int max_cnt;
+  if (threadIdx.x == 0) max_cnt = 0;
+  __syncthreads();
   const int e = threadIdx.x;
   // per expert: its total over the chunks, then (once the expert offsets are known) the chunk bases;
   // eight independent loads in flight per round in both passes (a serial chain of loads, or a
@@ -118,6 +121,7 @@ __global__ __launch_bounds__(512) void scan_kernel(const int32_t* __restrict__ c
       for (int u = 0; u < 8; ++u) cnt += c0 + u < nchunks ? chunk_counts[(int64_t)(c0 + u) * E + e] : 0;
     }
   }
+  if (pick_rows > 0 && cnt > 0) atomicMax(&max_cnt, cnt);  // read after the scan's barriers
   int total;
   const int off = block_exclusive_scan(cnt, wsum, &total);
   if (e < E) {
@@ -139,6 +143,9 @@ __global__ __launch_bounds__(512) void scan_kernel(const int32_t* __restrict__ c
   // the shared expert's tiles cover all N tokens, in token order
   build_tiles(t0, e < E, e, cnt, off, N, n_shared_problem, wsum);
   build_tiles(t1, e < E, e, cnt, off, N, n_shared_problem, wsum);
+  // both lists built (t0 of 16-row tiles, t1 of 256-row tiles): empty the one whose kernels do not run
+  // (thread 0 wrote both counts above)
+  if (pick_rows > 0 && threadIdx.x == 0) *(max_cnt <= pick_rows ? t1.n_tiles : t0.n_tiles) = 0;
 }
 
 // Stable placement of one chunk: rounds of PL pairs (in pair order); inside a round, a pair's
@@ -246,9 +253,9 @@ hipError_t launch_count(const int32_t* idx, int64_t N, int k, int E, int32_t* ch
 
 hipError_t launch_scan(const int32_t* chunk_counts, int nchunks, int64_t N, int k, int E, int n_shared_problem,
                        int32_t* counts, int32_t* offsets, int32_t* chunk_base, TileSpec t0, TileSpec t1,
-                       hipStream_t s) {
+                       int pick_rows, hipStream_t s) {
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(512), 0, s, chunk_counts, nchunks, N, k, E, n_shared_problem, counts,
-                     offsets, chunk_base, t0, t1);
+                     offsets, chunk_base, t0, t1, pick_rows);
   return hipGetLastError();
 }
 

@@ -153,6 +153,29 @@ int gemm_bm(int dtype, int64_t N, int k, int E) {
   return 256;                                           // prefill kernels, 256-row tiles
 }
 
+#ifndef MOE_PICK_BAND_ROWS
+#define MOE_PICK_BAND_ROWS 12  // average rows per expert below which the kernel choice is left to the device
+#endif
+#ifndef MOE_PICK_MAX_ROWS
+#define MOE_PICK_MAX_ROWS 24  // largest expert's rows up to which such a batch runs the decode kernels
+#endif
+
+// Between MOE_DECODE_ROWS and MOE_PICK_BAND_ROWS rows per expert on average the better kernel depends on
+// how the rows spread over the experts, which only the device knows: the forward builds both a 16-row
+// and a 256-row tile list, and the scan kernel empties the one not taken (the decode list when the
+// largest expert has more than MOE_PICK_MAX_ROWS rows). Measured (layer ms, prefill against decode
+// kernels): uniform routing, GLM-5 weights N = 128 / 192 / 256: 3.00 / 3.18 / 3.24 against 2.70 / 2.93 /
+// 3.16 (largest expert 13 / 17 / 23 rows), the 288-expert shape N = 192 / 256: 2.65 / 2.80 against
+// 2.24 / 2.42 (20 / 24 rows); skewed GLM-4.5 routing N = 96 / 128 (largest expert 51 / 66 rows): 0.47 /
+// 0.51 against 0.65 / 0.82; and from ~12 rows per expert the prefill kernels lead under uniform routing
+// too (GLM-5 N = 384, 28 rows: 3.39 against 3.98).
+int device_pick_rows(int dtype, int64_t N, int k, int E) {
+  if (dtype != MOE_BF16) return 0;
+  const int64_t pairs = N * k;
+  if (pairs < (int64_t)MOE_DECODE_ROWS * E || pairs >= (int64_t)MOE_PICK_BAND_ROWS * E) return 0;
+  return MOE_PICK_MAX_ROWS;
+}
+
 #ifndef MOE_SMALL_EXPERT_ROWS
 #define MOE_SMALL_EXPERT_ROWS 128  // 256-row tiles: experts with at most half a tile of rows
 #endif

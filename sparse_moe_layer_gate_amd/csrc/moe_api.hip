@@ -50,6 +50,7 @@ struct Workspace {
   RouterPlan rp;
   int64_t max_tiles0, max_tiles1;
   int bm0, bm1;
+  int pick;  // > 0: tiles0 holds 16-row and tiles1 256-row tiles, and the scan kernel picks one of them
 };
 
 Workspace layout(const moe_config* c, int64_t N) {
@@ -59,8 +60,9 @@ Workspace layout(const moe_config* c, int64_t N) {
   const int64_t es = c->dtype == MOE_F32 ? 4 : 2;
   const int64_t nchunks = (N + kDispatchChunk - 1) / kDispatchChunk;
   const int shp = c->n_shared_experts > 0;
-  w.bm0 = gemm_bm(c->dtype, N, (int)k, (int)E);
-  w.bm1 = w.bm0;
+  w.pick = device_pick_rows(c->dtype, N, (int)k, (int)E);
+  w.bm0 = w.pick ? 16 : gemm_bm(c->dtype, N, (int)k, (int)E);
+  w.bm1 = w.pick ? 256 : w.bm0;
   w.max_tiles0 = max_tiles(N, (int)k, (int)E, shp, w.bm0);
   w.max_tiles1 = max_tiles(N, (int)k, (int)E, shp, w.bm1);
   w.rp = router_plan(c->dtype, N, (int)D, (int)E);
@@ -197,9 +199,32 @@ moe_status dispatch_impl(const moe_config* c, int64_t N, const int32_t* idx, int
   TileSpec t1{L.bm1, at<Tile>(ws, L.tiles1), ntiles + 1, small_expert_rows(c->dtype, L.bm1), ntiles + 10};
   MOE_TRY(ST_COUNT, launch_count(idx, N, k, E, at<int32_t>(ws, L.chunk_counts), s));
   MOE_TRY(ST_SCAN, launch_scan(at<int32_t>(ws, L.chunk_counts), nchunks, N, k, E, c->n_shared_experts > 0, counts,
-                               offsets, at<int32_t>(ws, L.chunk_base), t0, t1, s));
+                               offsets, at<int32_t>(ws, L.chunk_base), t0, t1, L.pick, s));
   MOE_TRY(ST_PLACE, launch_place(idx, N, k, E, at<int32_t>(ws, L.chunk_base), sorted_pair, inv_row, s));
   return MOE_OK;
+}
+
+// One grouped GEMM over the workspace's tile list `list` (0 or 1), with the 8 work counters at `ctr` in
+// the count block.
+hipError_t grouped_gemm(bool gate_up, int dtype, GroupedArgs g, void* ws, const Workspace& L, int list, int ctr,
+                        hipStream_t s) {
+  int32_t* block = at<int32_t>(ws, L.ntiles);  // the two tile counts, then the work counters
+  g.tiles = at<Tile>(ws, list ? L.tiles1 : L.tiles0);
+  g.n_tiles = block + list;
+  g.work_ctr = block + ctr;
+  g.bm = list ? L.bm1 : L.bm0;
+  const int64_t max_tile_count = list ? L.max_tiles1 : L.max_tiles0;
+  return gate_up ? launch_gate_up(dtype, g, max_tile_count, s) : launch_down(dtype, g, max_tile_count, s);
+}
+
+// gate_up runs over list 0 (counters 2..9), down over list 1 (counters 10..17). When the device picks the
+// kernel (L.pick), both GEMMs launch the decode kernel over list 0 and the prefill kernel over list 1, and
+// the scan kernel has emptied one of the two lists, whose launch then does nothing.
+hipError_t gemm_stage(bool gate_up, int dtype, const GroupedArgs& g, void* ws, const Workspace& L, hipStream_t s) {
+  const int ctr = gate_up ? 2 : 10;
+  if (!L.pick) return grouped_gemm(gate_up, dtype, g, ws, L, gate_up ? 0 : 1, ctr, s);
+  const hipError_t e = grouped_gemm(gate_up, dtype, g, ws, L, 0, ctr, s);
+  return e != hipSuccess ? e : grouped_gemm(gate_up, dtype, g, ws, L, 1, ctr, s);
 }
 
 // Routed experts, shared expert and combine for routing (idx, w) already dispatched into the workspace.
@@ -217,24 +242,16 @@ moe_status experts_impl(const moe_config* cfg, int64_t N, const void* x, const m
   g.swiglu_limit = cfg->swiglu_limit;
   g.gather_rows = N;
   // gate_up + SwiGLU: routed rows gather x through sorted_pair; the shared expert reads x in order
-  g.tiles = at<Tile>(ws, L.tiles0);
-  g.n_tiles = at<int32_t>(ws, L.ntiles);
-  g.work_ctr = at<int32_t>(ws, L.ntiles) + 2;
-  g.bm = L.bm0;
   g.prob[0] = ExpertProblem{x, D, 1, wt->gate_up, (const char*)wt->gate_up + es * (int64_t)d * D, 2LL * d * D, D, d,
                             at<void>(ws, L.H), d, 0};
   if (shared)
     g.prob[1] = ExpertProblem{x, D, 0, wt->sh_gate, wt->sh_up, 0, D, dsh, at<void>(ws, L.Hsh), dsh, 0};
-  MOE_TRY(ST_GATE_UP, launch_gate_up(cfg->dtype, g, L.max_tiles0, s));
+  MOE_TRY(ST_GATE_UP, gemm_stage(true, cfg->dtype, g, ws, L, s));
   // down + mixture weight (routed) / weight 1 (shared)
-  g.tiles = at<Tile>(ws, L.tiles1);
-  g.n_tiles = at<int32_t>(ws, L.ntiles) + 1;
-  g.work_ctr = at<int32_t>(ws, L.ntiles) + 10;
-  g.bm = L.bm1;
   g.prob[0] = ExpertProblem{at<void>(ws, L.H), d, 0, wt->down, nullptr, (int64_t)D * d, d, D, at<void>(ws, L.Y), D, 1};
   if (shared)
     g.prob[1] = ExpertProblem{at<void>(ws, L.Hsh), dsh, 0, wt->sh_down, nullptr, 0, dsh, D, at<void>(ws, L.Ysh), D, 0};
-  MOE_TRY(ST_DOWN, launch_down(cfg->dtype, g, L.max_tiles1, s));
+  MOE_TRY(ST_DOWN, gemm_stage(false, cfg->dtype, g, ws, L, s));
   const float alpha_out = cfg->alpha_on_output ? cfg->routed_scaling_factor : 1.0f;
   MOE_TRY(ST_COMBINE, launch_combine(cfg->dtype, at<void>(ws, L.Y), shared ? at<void>(ws, L.Ysh) : nullptr,
                                      at<int32_t>(ws, L.inv_row), N, k, D, alpha_out, y, s));

@@ -98,7 +98,7 @@ struct TileSpec {
 hipError_t launch_count(const int32_t* idx, int64_t N, int k, int E, int32_t* chunk_counts, hipStream_t s);
 hipError_t launch_scan(const int32_t* chunk_counts, int nchunks, int64_t N, int k, int E, int n_shared_problem,
                        int32_t* counts, int32_t* offsets, int32_t* chunk_base, TileSpec t0, TileSpec t1,
-                       hipStream_t s);
+                       int pick_rows, hipStream_t s);
 // Tile lists of a single dense problem over N rows (the dense FFN).
 hipError_t launch_dense_tiles(int64_t N, TileSpec t0, TileSpec t1, hipStream_t s);
 hipError_t launch_place(const int32_t* idx, int64_t N, int k, int E, const int32_t* chunk_base, int32_t* sorted_pair,
@@ -168,6 +168,7 @@ __device__ inline int64_t xcd_logical_block(int64_t nvalid) {
 int64_t max_tiles(int64_t N, int k, int E, int n_shared_problem, int bm);
 int gemm_bm(int dtype, int64_t N, int k, int E);  // rows per tile the forward will use
 int small_expert_rows(int dtype, int bm);         // TileSpec::small_max for a list of bm-row tiles
+int device_pick_rows(int dtype, int64_t N, int k, int E);  // > 0: both tile lists, the scan picks
 hipError_t launch_gate_up(int dtype, const GroupedArgs& a, int64_t max_tile_count, hipStream_t s);
 hipError_t launch_down(int dtype, const GroupedArgs& a, int64_t max_tile_count, hipStream_t s);
 hipError_t launch_bf16_prefill(bool gate_up, int bm, const GroupedArgs& a, int64_t max_tile_count, hipStream_t s);

@@ -101,7 +101,7 @@ def test_device_generator_matches_host():
 
 def test_forward_reuses_workspace():
     """One workspace, sized for the largest batch, serves calls of falling and rising N (256-row tiles,
-    then 16-row tiles, then 256-row tiles again): every output equals that of a call with a fresh
+    then 16-row tiles, then both lists, then 256-row tiles again): every output equals that of a call with a fresh
     workspace, bit for bit. Each call rebuilds the tile lists and zeroes the prefill kernels' work
     counters, whatever the workspace held."""
     import torch
@@ -114,10 +114,36 @@ def test_forward_reuses_workspace():
     x_dev = H.to_device(synth.x_host(w))
     cfg = moe.config_of(w)
     ws = moe.alloc_workspace(cfg, w.N)
-    for n in (1500, 700, 10, 1500):  # 10 tokens: 40 pairs on 16 experts run the 16-row tiles
+    # 10 tokens: 40 pairs on 16 experts run the 16-row tiles; 20 and 30 tokens (5 and 7.5 rows per
+    # expert) build both lists and let the device pick
+    for n in (1500, 700, 10, 30, 20, 1500):
         print(f"[reuse] N={n}", flush=True)
         y = torch.empty((n, w.D), dtype=x_dev.dtype, device="cuda")
         moe.moe_forward(cfg, n, x_dev[:n], dev, y, ws)
         torch.cuda.synchronize()
         y_fresh, _, _, _ = H.gpu_forward(w, x_dev[:n], dev)
         assert np.array_equal(H.to_host(y), y_fresh), n
+
+
+# 4 to 12 rows per expert on average (bf16): both tile lists are built and the scan kernel keeps the
+# 16-row list when the largest expert has at most 24 rows, else the 256-row list.
+PICK = [
+    (dict(N=100, D=320, E=64, G=1, TG=1, k=4, d=192, n_shared=1, alpha=2.5), "decode"),
+    (dict(N=120, D=320, E=64, G=1, TG=1, k=4, d=192, n_shared=1, alpha=2.5, skew=1.0), "prefill"),
+    (dict(N=100, D=128, E=512, G=64, TG=8, k=32, d=64, n_shared=1, alpha=2.5), None),
+]
+
+
+@pytest.mark.parametrize("case,kind", PICK, ids=lambda c: f"N{c['N']}-E{c['E']}" if isinstance(c, dict) else str(c))
+def test_forward_device_picked_kernels(case, kind):
+    w = replace(synth.WORKLOADS["tiny_fp32"], name="pick", dtype="bf16", seed=5, **case)
+    assert 4 * w.E <= w.N * w.k < 12 * w.E
+    print(f"[pick] {case} expect {kind}", flush=True)
+    wg, b, dev = H.device_weights(w, generate_on_device=False)
+    x = synth.x_host(w)
+    y, idx, wt, counts = H.gpu_forward(w, H.to_device(x), dev)
+    if kind == "decode":
+        assert counts.max() <= 24
+    elif kind == "prefill":
+        assert counts.max() > 24
+    H.check_forward(w, x, wg, b, y, idx, wt, counts, np.arange(w.N))
