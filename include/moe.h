@@ -106,7 +106,8 @@ typedef struct {
 moe_status moe_check_config(const moe_config* cfg);
 
 /* Host only. Bytes of workspace moe_forward and moe_dispatch need for N tokens (0 for an invalid
- * config). The size grows linearly in N. */
+ * config): the most any batch of at most N tokens needs, so the size never falls as N grows and a
+ * workspace sized for the largest batch serves every smaller one. */
 size_t moe_workspace_size(const moe_config* cfg, int64_t N);
 
 /* Router: gate GEMM + sigmoid, then group-restricted top-k and mixture weights ("Group Router").

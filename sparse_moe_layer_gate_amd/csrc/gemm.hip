@@ -176,6 +176,8 @@ int device_pick_rows(int dtype, int64_t N, int k, int E) {
   return MOE_PICK_MAX_ROWS;
 }
 
+int tile_plan_rows(int i) { return i == 0 ? MOE_DECODE_ROWS : MOE_PICK_BAND_ROWS; }
+
 #ifndef MOE_SMALL_EXPERT_ROWS
 #define MOE_SMALL_EXPERT_ROWS 128  // 256-row tiles: experts with at most half a tile of rows
 #endif

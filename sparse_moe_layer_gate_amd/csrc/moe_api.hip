@@ -2,6 +2,7 @@
 // workspace carve-up, and the launch sequence of the forward on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <vector>
 
@@ -297,7 +298,22 @@ moe_status moe_check_config(const moe_config* cfg) { return check_cfg(cfg); }
 
 size_t moe_workspace_size(const moe_config* cfg, int64_t N) {
   if (check_cfg(cfg) != MOE_OK || check_n(cfg, N) != MOE_OK) return 0;
-  return layout(cfg, N).total;
+  // layout(n).total is not monotone in n: the router's K split and the GEMM tile height change with n,
+  // and where they do the buffers they size can shrink by more than a token's worth. The size reported
+  // is the most any batch of at most N tokens needs, so a workspace sized for the largest batch serves
+  // every smaller one. Between the points where the plan changes form the size grows with n, so the
+  // candidates are N and the last n before each change: the multiples of the router's row block (its
+  // tile count, and with it the K split, changes there; from 512 row blocks on the split is 1) and the
+  // last n under each tile-height threshold.
+  size_t most = layout(cfg, N).total;
+  auto consider = [&](int64_t n) {
+    if (n >= 1 && n < N) most = std::max(most, layout(cfg, n).total);
+  };
+  const int64_t rb = router_rows_per_block(cfg->dtype);
+  for (int64_t m = 1; m <= 513 && m * rb < N; ++m) consider(m * rb);
+  const int64_t E = cfg->n_routed_experts, k = cfg->num_experts_per_tok;
+  for (int i = 0; i < 2; ++i) consider((tile_plan_rows(i) * E + k - 1) / k - 1);
+  return most;
 }
 
 moe_status moe_route(const moe_config* cfg, int64_t N, const void* x, const float* w_router, const float* e_bias,

@@ -80,6 +80,7 @@ struct RouterPlan {
   int kchunk;  // hidden elements per split (a multiple of 32)
 };
 RouterPlan router_plan(int dtype, int64_t N, int D, int E);
+int router_rows_per_block(int dtype);  // token rows of one logits block (the plan changes at multiples)
 hipError_t launch_router_split(const float* wg, int E, int D, uint16_t* w3, hipStream_t s);
 hipError_t launch_logits(int dtype, const RouterPlan& p, const void* x, const float* wg, const uint16_t* w3, int64_t N,
                          int D, int E, float* part, hipStream_t s);
@@ -169,6 +170,7 @@ int64_t max_tiles(int64_t N, int k, int E, int n_shared_problem, int bm);
 int gemm_bm(int dtype, int64_t N, int k, int E);  // rows per tile the forward will use
 int small_expert_rows(int dtype, int bm);         // TileSpec::small_max for a list of bm-row tiles
 int device_pick_rows(int dtype, int64_t N, int k, int E);  // > 0: both tile lists, the scan picks
+int tile_plan_rows(int i);  // i = 0, 1: rows per expert (pairs / E) where the tile lists change form
 hipError_t launch_gate_up(int dtype, const GroupedArgs& a, int64_t max_tile_count, hipStream_t s);
 hipError_t launch_down(int dtype, const GroupedArgs& a, int64_t max_tile_count, hipStream_t s);
 hipError_t launch_bf16_prefill(bool gate_up, int bm, const GroupedArgs& a, int64_t max_tile_count, hipStream_t s);

@@ -424,6 +424,8 @@ __global__ __launch_bounds__(256) void select_kernel(float* __restrict__ scores,
 #define MOE_ROUTER_BLOCKS 256  // blocks the bf16 gate GEMM aims for (the K range splits until then)
 #endif
 
+int router_rows_per_block(int dtype) { return dtype == MOE_BF16 ? RB_BM : LG_BM; }
+
 RouterPlan router_plan(int dtype, int64_t N, int D, int E) {
   RouterPlan p;
   p.split = dtype == MOE_BF16;

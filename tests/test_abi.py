@@ -5,6 +5,7 @@ import os
 import re
 from dataclasses import replace
 
+import numpy as np
 import pytest
 
 import sparse_moe_layer_gate_amd as moe
@@ -43,6 +44,16 @@ def test_workspace_size_small_and_monotone():
         sizes = [moe.moe_workspace_size(cfg, n) for n in (0, 1, 2, 31, 32, 1000)]
         assert all(a <= b for a, b in zip(sizes, sizes[1:])), (name, sizes)
     assert moe.moe_workspace_size(cfg, -1) == 0
+
+
+@pytest.mark.parametrize("name", ["glm5_decode", "glm53_flash_decode", "glm45_prefill_skewed", "tiny_fp32"])
+def test_workspace_size_never_falls(name):
+    """Every N from 1 to 4,500: the reported size never falls as N grows (the router's K split and the
+    GEMM tile height change with N, and the buffers they size with them), so one workspace sized for
+    the largest batch serves every smaller one."""
+    cfg = moe.config_of(synth.WORKLOADS[name])
+    sizes = np.array([moe.moe_workspace_size(cfg, n) for n in range(1, 4501)], dtype=np.int64)
+    assert (np.diff(sizes) >= 0).all(), int(np.argmin(np.diff(sizes))) + 1
 
 
 @pytest.mark.parametrize("field,value,status", [
