@@ -114,17 +114,49 @@ def gpu_forward_routed(w: synth.Workload, x_dev, dev_w: dict, idx: np.ndarray, w
     return out
 
 
+# Constant of the statistical float32 accumulation bound below (in standard-deviation-like units of the
+# rounding random walk). Sequential float32 accumulation of the 3 D exact products, the order with the
+# most roundings, stays under 2.6 of these units on 64 tokens of the GLM-4.5 / Air / GLM-5 shapes; a
+# router evaluated with W_g rounded to bfloat16 lands at 100-700 units (median) on the same inputs.
+ROUTER_ACC_C = 8.0
+U32 = 2.0 ** -24  # unit roundoff of float32
+
+
+def logit_tolerance(w: synth.Workload, x: np.ndarray, wg: np.ndarray) -> np.ndarray:
+    """Bound on |r_gpu - r_oracle| per (token, expert) for a float32 gate ("Group Router", How it works:
+    the gate is evaluated in float32). The device logit is a float32 accumulation of at most 3 D exact
+    products (bf16 activations times the three bf16 pieces of the router weight; D fused products for
+    float32 activations). Each rounding adds at most u times a partial sum, and for products of random
+    sign the partial sums grow like a random walk, so the accumulated error is of order
+    sqrt(n) u ||x o W||_2 with n = 3 D roundings -- far tighter than the worst-case n u sum |x W|, and
+    a bfloat16 gate (relative error 2^-9 per weight) exceeds it by two orders of magnitude. The
+    oracle's own rounding of r adds one float32 spacing."""
+    xf = as_f32(x).astype(np.float64)
+    w64 = np.asarray(wg, np.float64)
+    l2 = np.sqrt((xf * xf) @ (w64 * w64).T)
+    r = xf @ w64.T
+    return ROUTER_ACC_C * math.sqrt(3 * w.D) * U32 * l2 + np.spacing(np.abs(r).astype(np.float32)).astype(np.float64)
+
+
 def score_tolerance(w: synth.Workload, x: np.ndarray, wg: np.ndarray) -> np.ndarray:
-    """Per-element bound on |s_gpu - s_oracle|. The device logit is a float32 accumulation of at most 3 D
-    exact products (bf16 activations times the three bf16 pieces of the router weight; D products for
-    float32 activations) in partial sums that are then added: |dr| <= 3 D u sum_t |x_t W_t| + ulp(r)
-    (u = 2^-24, the standard recursive-summation bound). The sigmoid has slope <= 1/4; 4 ulp of [0, 1]
-    cover the device exp and divide."""
-    xa = np.abs(as_f32(x)).astype(np.float64)
-    wa = np.abs(wg).astype(np.float64)
-    absdot = xa @ wa.T
-    u = 2.0 ** -24
-    return 0.25 * (3 * w.D * u * absdot + absdot * u) + 4 * u
+    """Bound on |s_gpu - s_oracle| per (token, expert): the logit bound through the sigmoid's slope
+    s (1 - s) at the exact logit, plus 4 float32 spacings of s for the device exponential and divide,
+    plus 2^-125: below about 1e-38 (logits under -87) a float32 exponential overflows or the quotient
+    leaves the normal range, where the oracle's double sigmoid still rounds to a subnormal."""
+    xf = as_f32(x).astype(np.float64)
+    r = xf @ np.asarray(wg, np.float64).T
+    with np.errstate(over="ignore"):
+        s = 1.0 / (1.0 + np.exp(-r))
+    return (s * (1.0 - s) * logit_tolerance(w, x, wg) + 4 * np.spacing(s.astype(np.float32)).astype(np.float64)
+            + 2.0 ** -125)
+
+
+def within_near_tie(margin: np.ndarray, ds: np.ndarray) -> np.ndarray:
+    """Whether a routing difference is explained by score errors of at most ds per expert: a decision
+    between two experts flips only if their s' gap is at most 2 ds, one between two groups (each group
+    score sums two s') only if the gap is at most 4 ds, plus a few float32 spacings of the s' and group
+    score roundings (values below 4). The oracle's margin is the smallest such gap."""
+    return margin <= 4.0 * ds + 2.0 ** -20
 
 
 def sample_tokens(N: int, count: int, seed: int = 0) -> np.ndarray:
@@ -132,6 +164,33 @@ def sample_tokens(N: int, count: int, seed: int = 0) -> np.ndarray:
     fixed = [0, N - 1, N // 2]
     extra = rng.choice(N, size=min(count, N), replace=False)
     return np.unique(np.concatenate([np.array(fixed[: min(3, N)]), extra]))[:max(count, 1) + 3]
+
+
+def tile_cover_tokens(w: synth.Workload, idx: np.ndarray, bm: int):
+    """Tokens that put at least one row into every row tile of the grouped GEMMs' tile lists: for each
+    routed expert (rows = its (token, slot) pairs in ascending token order, as dispatch places them) and
+    for the shared expert (rows = tokens in order), the first and last row of every bm-row tile, so each
+    expert's partial last tile is included. Returns (tokens, tiles, covered)."""
+    flat = idx.ravel()
+    order = np.argsort(flat, kind="stable")  # pairs grouped by expert, ascending pair index inside
+    counts = np.bincount(flat, minlength=w.E)
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    tok_of_row = order // w.k
+    picks = []
+    tiles = []  # (first row token set) per tile, for the coverage count
+    for e in range(w.E):
+        for t0 in range(0, int(counts[e]), bm):
+            rows = tok_of_row[offsets[e] + t0: offsets[e] + min(t0 + bm, int(counts[e]))]
+            picks += [rows[0], rows[-1]]
+            tiles.append(rows)
+    if w.n_shared > 0:
+        for t0 in range(0, w.N, bm):
+            rows = np.arange(t0, min(t0 + bm, w.N))
+            picks += [rows[0], rows[-1]]
+            tiles.append(rows)
+    tokens = np.unique(np.asarray(picks, np.int64))
+    covered = sum(bool(np.intersect1d(rows, tokens).size) for rows in tiles)
+    return tokens, len(tiles), covered
 
 
 def rel_err(y: np.ndarray, ref: np.ndarray) -> float:
@@ -158,13 +217,14 @@ def std_of(fan_in):
 
 
 def check_forward(w, x, wg, b, y, idx, wt, counts, tokens):
-    """Routing check over all tokens, output check over `tokens`."""
+    """Routing check over all tokens, output check over `tokens`. A token's expert ids may differ from
+    the oracle's only at a near-tie: the oracle's decision margin within what the score bound can flip."""
     s_ref = oracle.scores(w, x, wg)
     idx_ref, w_ref = oracle.select(w, s_ref, b)
     margin = oracle.select_margin(w, s_ref, b)
     tol_s = score_tolerance(w, x, wg).max(axis=1)
     differ = np.any(idx != idx_ref, axis=1)
-    assert np.all(margin[differ] <= 2 * tol_s[differ]), "a routing difference away from a near-tie"
+    assert np.all(within_near_tie(margin[differ], tol_s[differ])), "a routing difference away from a near-tie"
     assert np.array_equal(counts, np.bincount(idx.ravel(), minlength=w.E))
     same = ~differ
     # weights from the GPU's own scores: the score bound t propagated through w_i = alpha s_i / S,
@@ -186,6 +246,7 @@ def check_forward(w, x, wg, b, y, idx, wt, counts, tokens):
     table = expert_table(w, r_idx[tokens].ravel())
     y_ref = oracle.forward_tokens(w, tokens, x, table, r_idx, r_w)
     err = rel_err(as_f32(y[tokens]), y_ref)
-    print(f"  {w.name}: tokens={tokens.size} differ={int(differ.sum())} rel_err={err:.3g}", flush=True)
+    print(f"  {w.name}: tokens={tokens.size} differ={int(differ.sum())} "
+          f"max_w_dev={dev_w[same].max() if same.any() else 0:.3g} rel_err={err:.3g}", flush=True)
     assert err <= TOL[w.dtype], err
     return err

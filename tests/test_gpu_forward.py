@@ -1,10 +1,11 @@
 """GPU parity of the whole layer (moe_forward through the C ABI) against the oracle.
 
 Protocol: the GPU's expert ids must equal the oracle's for every token whose oracle decision gap exceeds
-the score error bound (near-ties may flip); the output is compared per token with the oracle evaluated
-on the oracle's routing, or on the GPU's routing for the near-tie tokens, at max|dy| / max|y| <= 1e-4
-(float32 layers) or <= 2e-2 (bfloat16 layers). Full-size workloads are checked on sampled tokens (every
-token's routing is checked); small shapes that span several tiles and ragged tails are checked whole.
+what the float32 score bound can flip (near-ties may flip); the output is compared per token with the
+oracle evaluated on the oracle's routing, or on the GPU's routing for the near-tie tokens, at
+max|dy| / max|y| <= 1e-4 (float32 layers) or <= 2e-2 (bfloat16 layers). Full-size workloads are checked
+on a token set that covers every row tile of both grouped GEMMs (every token's routing is checked);
+small shapes that span several tiles and ragged tails are checked whole.
 """
 from dataclasses import replace
 
@@ -20,14 +21,48 @@ pytestmark = pytest.mark.gpu
 
 @pytest.mark.parametrize("name", synth.WORKLOAD_ORDER)
 def test_forward_workload(name):
+    """Full-size workloads. Routing is checked on every token. The output is checked on every token of
+    the small batches, and elsewhere on a set of tokens that puts at least one row into every row tile
+    of both grouped GEMMs (each routed expert's 256-row tiles including its partial last one, and the
+    shared expert's tiles); a full output row spans every column tile of both GEMMs."""
     w = synth.WORKLOADS[name]
     print(f"[forward] {name} N={w.N} D={w.D} E={w.E} k={w.k} d={w.d}", flush=True)
     big = w.E * w.d * w.D > 50_000_000
     wg, b, dev = H.device_weights(w, generate_on_device=big)
     x = synth.x_host(w)
-    y, idx, wt, counts = H.gpu_forward(w, H.to_device(x), dev)
-    tokens = H.sample_tokens(w.N, 24 if big else w.N, seed=1)
+    x_dev = H.to_device(x)
+    y, idx, wt, counts = H.gpu_forward(w, x_dev, dev)
+    # the forward's routing is moe_route's, bit for bit, and is what the oracle's selection makes of the
+    # scores moe_route writes
+    s_g, idx_r, wt_r = route_gpu(w, x_dev, dev)
+    assert np.array_equal(idx, idx_r) and np.array_equal(wt.view(np.uint32), wt_r.view(np.uint32))
+    idx_s, wt_s = oracle.select(w, s_g, b)
+    assert np.array_equal(idx_s, idx) and np.array_equal(wt_s.view(np.uint32), wt.view(np.uint32))
+    if w.N <= 512:
+        tokens = np.arange(w.N)
+    else:
+        bm = 16 if w.N * w.k < 4 * w.E else 256
+        tokens, n_tiles, covered = H.tile_cover_tokens(w, idx, bm)
+        print(f"  tile coverage: {covered}/{n_tiles} tiles of {bm} rows ({100.0 * covered / n_tiles:.1f}%), "
+              f"{tokens.size} tokens", flush=True)
+        assert covered == n_tiles
     H.check_forward(w, x, wg, b, y, idx, wt, counts, tokens)
+
+
+def route_gpu(w, x_dev, dev):
+    """moe_route on device inputs; returns (scores, idx, wt) as host arrays."""
+    import torch
+
+    import sparse_moe_layer_gate_amd as moe
+
+    cfg = moe.config_of(w)
+    N = x_dev.shape[0]
+    s = torch.empty((N, w.E), dtype=torch.float32, device="cuda")
+    idx = torch.empty((N, w.k), dtype=torch.int32, device="cuda")
+    wt = torch.empty((N, w.k), dtype=torch.float32, device="cuda")
+    moe.moe_route(cfg, N, x_dev, dev["w_router"], dev["e_bias"], s, idx, wt, workspace=moe.alloc_workspace(cfg, N))
+    torch.cuda.synchronize()
+    return H.to_host(s), H.to_host(idx), H.to_host(wt)
 
 
 SMALL = [

@@ -1,8 +1,10 @@
 """GPU parity of the router and the dispatch against the oracle, through the C ABI.
 
 Bar: given the oracle's float32 scores, the GPU's expert ids and weights are bit-identical
-(moe_route with MOE_ROUTE_SCORES_IN); the GPU's own scores are within the float32 accumulation bound
-of the oracle's; counts, offsets, sorted_pair and inv_row are bit-identical.
+(moe_route with MOE_ROUTE_SCORES_IN); the GPU's own scores are within a float32 accumulation bound of
+the oracle's (one a bfloat16 gate fails, tests/test_router_bound.py); the GPU's ids and weights are
+bit-identical to the oracle's selection applied to the scores the GPU wrote, and differ from the
+oracle's routing only at near-ties; counts, offsets, sorted_pair and inv_row are bit-identical.
 """
 from dataclasses import replace
 
@@ -82,23 +84,37 @@ def test_selection_bitexact_tie_rich(case, grid):
     assert np.array_equal(wt.view(np.uint32), w_ref.view(np.uint32))
 
 
+def check_scores(w, x, wg, b, s, idx, wt):
+    """The GPU router's float32 scores against the oracle's, and its routing against both the oracle's
+    routing and the oracle's selection applied to the GPU's own scores."""
+    s_ref = oracle.scores(w, x, wg)
+    tol = H.score_tolerance(w, x, wg)
+    err = np.abs(s.astype(np.float64) - s_ref)
+    ratio = err / tol
+    print(f"  {w.name}: max |ds| {err.max():.3g}, max |ds| / bound {ratio.max():.3g}", flush=True)
+    assert np.all(err <= tol), f"max err {err.max():.3g}, worst ratio {ratio.max():.3g}"
+    # the ids and weights are exactly what the selection makes of the scores the kernel wrote
+    idx_s, wt_s = oracle.select(w, s, b)
+    assert np.array_equal(idx, idx_s)
+    assert np.array_equal(wt.view(np.uint32), wt_s.view(np.uint32))
+    # against the oracle's routing: differences only where the oracle's decision margin is within what
+    # this token's actual score errors can flip
+    idx_ref, _ = oracle.select(w, s_ref, b)
+    margin = oracle.select_margin(w, s_ref, b)
+    differ = np.any(idx != idx_ref, axis=1)
+    if differ.any():
+        print(f"  {int(differ.sum())} tokens differ, oracle margins {np.sort(margin[differ])[:8]}", flush=True)
+    assert np.all(H.within_near_tie(margin[differ], err.max(axis=1)[differ]))
+
+
 @pytest.mark.parametrize("name", ALL)
 def test_scores_within_bound(name):
     w = synth.WORKLOADS[name]
     print(f"[scores] {name}", flush=True)
     x = synth.x_host(w)
     wg, b = synth.router_host(w)
-    s_ref = oracle.scores(w, x, wg)
     s, idx, wt = _route_gpu(w, w.N, x_host=x, wg=wg, b=b)
-    tol = H.score_tolerance(w, x, wg)
-    err = np.abs(s.astype(np.float64) - s_ref)
-    assert np.all(err <= tol), f"max err {err.max():.3g}, worst ratio {(err / tol).max():.3g}"
-    # routing from the GPU's scores equals the oracle's except where the oracle's decision gap is
-    # within twice the score error bound
-    idx_ref, _ = oracle.select(w, s_ref, b)
-    margin = oracle.select_margin(w, s_ref, b)
-    differ = np.any(idx != idx_ref, axis=1)
-    assert np.all(margin[differ] <= 2 * tol.max(axis=1)[differ])
+    check_scores(w, x, wg, b, s, idx, wt)
 
 
 # Router GEMM tile shapes: E past 256 and not a multiple of 32 (two blocks of five 32-expert tiles, the
@@ -118,15 +134,8 @@ def test_scores_within_bound_gemm_shapes(case):
     print(f"[scores] {case}", flush=True)
     x = synth.x_host(w)
     wg, b = synth.router_host(w)
-    s_ref = oracle.scores(w, x, wg)
     s, idx, wt = _route_gpu(w, w.N, x_host=x, wg=wg, b=b)
-    tol = H.score_tolerance(w, x, wg)
-    err = np.abs(s.astype(np.float64) - s_ref)
-    assert np.all(err <= tol), f"max err {err.max():.3g}, worst ratio {(err / tol).max():.3g}"
-    idx_ref, _ = oracle.select(w, s_ref, b)
-    margin = oracle.select_margin(w, s_ref, b)
-    differ = np.any(idx != idx_ref, axis=1)
-    assert np.all(margin[differ] <= 2 * tol.max(axis=1)[differ])
+    check_scores(w, x, wg, b, s, idx, wt)
 
 
 def _dispatch_gpu(w, idx):

@@ -260,3 +260,72 @@ def test_margin_detects_ties():
     m = oracle.select_margin(c, s, np.zeros(8, np.float32))
     assert m[0] == 0.0
     assert abs(m[1] - 0.2) < 1e-6
+
+
+def test_margin_golden_cases():
+    """Hand-derived cases (tests/golden/select_margin_cases.json) in which the group branch of the margin
+    (weakest kept group against the best discarded one) or the expert branch decides, with ties and a
+    bias that changes the group ranking."""
+    with open(os.path.join(GOLDEN, "select_margin_cases.json")) as f:
+        cases = json.load(f)["cases"]
+    for case in cases:
+        c = cfg(E=case["E"], G=case["G"], TG=case["TG"], k=case["k"])
+        s = np.array([case["s"]], np.float32)
+        b = np.array(case["b"], np.float32)
+        idx, _ = oracle.select(c, s, b)
+        m = oracle.select_margin(c, s, b)
+        assert idx[0].tolist() == case["idx"], case["name"]
+        assert m[0] == case["margin"], (case["name"], m[0])
+
+
+def brute_force_margin(c, s_row, b_row):
+    """The decision margin from sorted lists: group scores as the largest pairwise sum inside each group,
+    groups ranked by a sort on (score desc, index asc), the gap between the TG-th and (TG+1)-th; the
+    eligible experts' s' sorted descending, the gaps between consecutive values among the k + 1 best."""
+    sp = (s_row.astype(np.float32) + b_row.astype(np.float32)).astype(np.float32)
+    gs = c.E // c.G
+    gaps = []
+    kept = set(range(c.G))
+    if c.G > 1 and c.TG < c.G:
+        gscore = [max(np.float32(sp[i] + sp[j]) for i in range(g * gs, (g + 1) * gs)
+                      for j in range(g * gs, (g + 1) * gs) if i != j) for g in range(c.G)]
+        order = sorted(range(c.G), key=lambda g: (-float(gscore[g]), g))
+        kept = set(order[:c.TG])
+        gaps.append(float(gscore[order[c.TG - 1]]) - float(gscore[order[c.TG]]))
+    vals = sorted((float(sp[e]) for e in range(c.E) if e // gs in kept), reverse=True)[:c.k + 1]
+    gaps += [a - b for a, b in zip(vals[:-1], vals[1:])]
+    return min(gaps)
+
+
+@pytest.mark.parametrize("E,G,TG,k,grid", [(16, 4, 2, 4, False), (16, 4, 2, 4, True), (12, 3, 2, 3, False),
+                                           (32, 8, 3, 5, True), (24, 6, 5, 6, False), (12, 1, 1, 3, False),
+                                           (16, 8, 4, 3, True)])
+def test_margin_matches_sorted_definition(E, G, TG, k, grid):
+    c = cfg(E=E, G=G, TG=TG, k=k)
+    rng = np.random.default_rng(E * 7 + G * 3 + k + grid)
+    N = 60
+    if grid:
+        s = (rng.integers(0, 17, (N, E)) / 16.0).astype(np.float32)
+        b = (rng.integers(-2, 3, E) / 16.0).astype(np.float32)
+    else:
+        s = rng.uniform(0, 1, (N, E)).astype(np.float32)
+        b = rng.uniform(-0.05, 0.05, E).astype(np.float32)
+    m = oracle.select_margin(c, s, b)
+    for n in range(N):
+        assert m[n] == brute_force_margin(c, s[n], b), n
+
+
+def test_margin_is_robustness_radius():
+    """Perturbing every score by less than a quarter of the token's margin (a group score sums two s')
+    leaves the chosen experts and their slot order unchanged."""
+    c = cfg(E=16, G=4, TG=2, k=4)
+    rng = np.random.default_rng(5)
+    N = 400
+    s = rng.uniform(0, 1, (N, c.E)).astype(np.float32)
+    b = rng.uniform(-0.05, 0.05, c.E).astype(np.float32)
+    m = oracle.select_margin(c, s, b)
+    idx, _ = oracle.select(c, s, b)
+    for trial in range(5):
+        delta = rng.uniform(-1, 1, s.shape) * (0.24 * m)[:, None]
+        idx2, _ = oracle.select(c, (s + delta).astype(np.float32), b)
+        assert np.array_equal(idx, idx2)
