@@ -94,11 +94,13 @@ def _find(dirpath, suffix):
 def profile_summary(pdir: str, workload: str, decode: bool) -> str:
     """Markdown summary of a profiling directory laid out as
          trace/        rocprofv3 --kernel-trace --stats -f csv (this bench, this workload)
-         FETCH_SIZE/   rocprofv3 --pmc FETCH_SIZE -f csv   (this bench, this workload)
-         WRITE_SIZE/   rocprofv3 --pmc WRITE_SIZE -f csv
+         FETCH_SIZE/   rocprofv3 --pmc FETCH_SIZE -f csv   (this bench, this workload; optional)
+         WRITE_SIZE/   rocprofv3 --pmc WRITE_SIZE -f csv   (optional)
          FETCH_SIZE_copy/, WRITE_SIZE_copy/   the same counters on `bench.py --copy-calibration`
-       Byte counters are scaled by bytes-copied / counter-reading of the 1 GiB copy. Also writes the
-       dominant kernel's traffic file read by the benchmark."""
+         MFMA/         rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_INSTS_MFMA
+                       TCC_HIT_sum TCC_MISS_sum (optional)
+       Byte counters are scaled by bytes-copied / counter-reading of the 1 GiB copy; with them, also writes
+       the dominant kernel's traffic file read by the benchmark."""
     stats = _csv_rows(_find(os.path.join(pdir, "trace"), "_kernel_stats.csv"))
     lines = [f"# rocprofv3 kernel summary: {workload}", "",
              "| kernel | calls | avg ms | total % |", "|---|---:|---:|---:|"]
@@ -106,40 +108,72 @@ def profile_summary(pdir: str, workload: str, decode: bool) -> str:
         lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e6:.4f} | "
                      f"{float(r['Percentage']):.2f} |")
 
-    def per_kernel(sub):
+    def per_kernel(sub, counter=None):
         rows = _csv_rows(_find(os.path.join(pdir, sub), "_counter_collection.csv"))
         acc = {}
         for r in rows:
-            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]) * 1024.0)  # KiB -> B
+            if counter and r["Counter_Name"] != counter:
+                continue
+            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
         return {k: sum(v) / len(v) for k, v in acc.items()}
 
-    copy_bytes = float(1 << 30)
-    cf = per_kernel("FETCH_SIZE_copy")
-    cw = per_kernel("WRITE_SIZE_copy")
-    kcopy = next(k for k in cf if "copyBuffer" in k)
-    f_scale = copy_bytes / cf[kcopy]
-    w_scale = copy_bytes / cw[kcopy]
-    fetch, write = per_kernel("FETCH_SIZE"), per_kernel("WRITE_SIZE")
-    lines += ["", "## HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE, calibrated)", "",
-              f"Calibration on a 1 GiB device copy: FETCH_SIZE x {f_scale:.3f}, WRITE_SIZE x {w_scale:.3f}.", "",
-              "| kernel | fetch GB | write GB |", "|---|---:|---:|"]
-    for k in fetch:
-        if k in write:
-            lines.append(f"| `{k[:90]}` | {fetch[k] * f_scale / 1e9:.3f} | {write[k] * w_scale / 1e9:.3f} |")
-    dom = [k for a, b in KERNEL_NAMES["experts_gate_up_decode" if decode else "experts_gate_up"]
-           for k in fetch if a in k and b in k]
-    if dom:
-        k = dom[0]
-        fb, wb = fetch[k] * f_scale, write.get(k, 0.0) * w_scale
-        path = os.path.join(ROOT, "profiles", f"{DOMINANT}_{workload}_traffic.txt")
-        with open(path, "w") as f:
-            f.write(f"# {DOMINANT} on {workload}: HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE,\n"
-                    f"# each scaled by bytes / counter on a 1 GiB device copy (bench.py --copy-calibration).\n"
-                    f"# Commands: see profiles/README.md. Valid while kernel_source_sha matches.\n")
-            f.write(f"kernel: {k}\nkernel_source_sha: {kernel_source_hash()}\n")
-            f.write(f"fetch_scale: {f_scale:.4f}\nwrite_scale: {w_scale:.4f}\n")
-            f.write(f"fetch_bytes_per_launch: {fb:.0f}\nwrite_bytes_per_launch: {wb:.0f}\n")
-            f.write(f"hbm_bytes_per_launch: {fb + wb:.0f}\n")
+    if os.path.isdir(os.path.join(pdir, "FETCH_SIZE")):
+        copy_bytes = float(1 << 30)
+        cf = per_kernel("FETCH_SIZE_copy")
+        cw = per_kernel("WRITE_SIZE_copy")
+        kcopy = next(k for k in cf if "copyBuffer" in k)
+        f_scale = copy_bytes / (cf[kcopy] * 1024.0)  # counters in KiB
+        w_scale = copy_bytes / (cw[kcopy] * 1024.0)
+        fetch = {k: v * 1024.0 for k, v in per_kernel("FETCH_SIZE").items()}
+        write = {k: v * 1024.0 for k, v in per_kernel("WRITE_SIZE").items()}
+        lines += ["", "## HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE, calibrated)", "",
+                  f"Calibration on a 1 GiB device copy: FETCH_SIZE x {f_scale:.3f}, WRITE_SIZE x {w_scale:.3f}.", "",
+                  "| kernel | fetch GB | write GB |", "|---|---:|---:|"]
+        for k in fetch:
+            if k in write:
+                lines.append(f"| `{k[:90]}` | {fetch[k] * f_scale / 1e9:.3f} | {write[k] * w_scale / 1e9:.3f} |")
+        dom = [k for a, b in KERNEL_NAMES["experts_gate_up_decode" if decode else "experts_gate_up"]
+               for k in fetch if a in k and b in k]
+        if dom:
+            k = dom[0]
+            fb, wb = fetch[k] * f_scale, write.get(k, 0.0) * w_scale
+            path = os.path.join(ROOT, "profiles", f"{DOMINANT}_{workload}_traffic.txt")
+            with open(path, "w") as f:
+                f.write(f"# {DOMINANT} on {workload}: HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE,\n"
+                        f"# each scaled by bytes / counter on a 1 GiB device copy (bench.py --copy-calibration).\n"
+                        f"# Commands: see profiles/README.md. Valid while kernel_source_sha matches.\n")
+                f.write(f"kernel: {k}\nkernel_source_sha: {kernel_source_hash()}\n")
+                f.write(f"fetch_scale: {f_scale:.4f}\nwrite_scale: {w_scale:.4f}\n")
+                f.write(f"fetch_bytes_per_launch: {fb:.0f}\nwrite_bytes_per_launch: {wb:.0f}\n")
+                f.write(f"hbm_bytes_per_launch: {fb + wb:.0f}\n")
+
+    if os.path.isdir(os.path.join(pdir, "MFMA")):
+        rows = _csv_rows(_find(os.path.join(pdir, "MFMA"), "_counter_collection.csv"))
+        acc, dur = {}, {}
+        for r in rows:
+            k = r["Kernel_Name"]
+            acc.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            dur.setdefault(k, set()).add((r["Dispatch_Id"], int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+        lines += ["", "## MFMA utilisation and clock (rocprofv3 --pmc, one pass)", "",
+                  "GRBM_GUI_ACTIVE is summed over the 8 XCDs: cycles = GRBM_GUI_ACTIVE / 8, clock = cycles / "
+                  "duration. MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (cycles x 1024 SIMDs); at the measured clock "
+                  "that is busy x clock / 2.4 GHz of the 2,516.6 TFLOP/s bf16 peak. L2 hit = TCC_HIT / "
+                  "(TCC_HIT + TCC_MISS).", "",
+                  "| kernel | avg ms (under counters) | clock GHz | MFMA busy | implied TFLOP/s | L2 hit |",
+                  "|---|---:|---:|---:|---:|---:|"]
+        for k, c in acc.items():
+            mf = sum(c.get("SQ_VALU_MFMA_BUSY_CYCLES", [0.0]))
+            if mf == 0:
+                continue
+            n = len(c["GRBM_GUI_ACTIVE"])
+            cyc = sum(c["GRBM_GUI_ACTIVE"]) / n / 8
+            ns = sum(d for _, d in dur[k]) / len(dur[k])
+            busy = mf / n / (cyc * 1024)
+            ghz = cyc / ns
+            hit = sum(c.get("TCC_HIT_sum", [0.0])) / max(1.0, sum(c.get("TCC_HIT_sum", [0.0])) +
+                                                          sum(c.get("TCC_MISS_sum", [0.0])))
+            lines.append(f"| `{k[:70]}` | {ns / 1e6:.4f} | {ghz:.3f} | {busy:.1%} | "
+                         f"{busy * ghz / 2.4 * P_BF16 / 1e12:.0f} | {hit:.1%} |")
     return "\n".join(lines) + "\n"
 
 
@@ -213,6 +247,9 @@ def setup(w: synth.Workload):
     ws = moe.alloc_workspace(cfg, w.N)
     y = torch.empty_like(xd)
     counts = torch.empty(w.E, dtype=torch.int32, device="cuda")
+    if w.dtype == "bf16":
+        # the router weight's bf16 split is taken once per weight, as when a checkpoint is loaded
+        dev["w_router_prepared"] = moe.moe_router_prepare(cfg, dev["w_router"])
     weights = moe.weights_struct(cfg, dev)
     torch.cuda.synchronize()
     return {"cfg": cfg, "dev": dev, "weights": weights, "x": xd, "y": y, "ws": ws, "counts": counts}
@@ -325,27 +362,44 @@ def dense_bench(w, steps: int, warmup: int) -> dict:
     return out
 
 
-def cpu_baseline(w: synth.Workload, tokens: int) -> dict:
-    """The oracle (routing + per-expert loop form) on the first `tokens` tokens of the workload."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w: synth.Workload, tokens: int, runs: int = 3) -> dict:
+    """The oracle (routing + per-expert loop form) on the first `tokens` tokens of the workload: the
+    median wall time of `runs` runs, with the host's threads and CPU model."""
     import oracle
 
     sub = w.with_tokens(tokens)
     x = synth.x_host(w, 0, tokens)
     wg, b = synth.router_host(w)
-    t0 = time.perf_counter()
-    s = oracle.scores(sub, x, wg)
-    idx, wt = oracle.select(sub, s, b)
-    t_route = time.perf_counter() - t0
-    needed = {int(e): synth.expert_host(w, int(e)) for e in np.unique(idx)}
-    table = oracle.ExpertTable(sub, needed, synth.shared_host(w))
-    t1 = time.perf_counter()
-    oracle.forward_expert_loop(sub, x, table, idx, wt)
-    t_exp = time.perf_counter() - t1
-    secs = t_route + t_exp
-    return {"value": tokens / secs, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"first {tokens} of {w.N} tokens of {w.name}: oracle routing (double logits, float32 "
-                      f"selection) + per-expert loop form in double; weight generation not timed",
-            "seconds": secs}
+    times = []
+    table = None
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        s = oracle.scores(sub, x, wg)
+        idx, wt = oracle.select(sub, s, b)
+        t_route = time.perf_counter() - t0
+        if table is None:  # weight generation is set-up, not timed
+            needed = {int(e): synth.expert_host(w, int(e)) for e in np.unique(idx)}
+            table = oracle.ExpertTable(sub, needed, synth.shared_host(w))
+        t1 = time.perf_counter()
+        oracle.forward_expert_loop(sub, x, table, idx, wt)
+        times.append(t_route + time.perf_counter() - t1)
+    secs = float(np.median(times))
+    return {"value": round(tokens / secs, 2), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "cpu_model": cpu_model(), "runs": runs, "seconds_median": round(secs, 3),
+            "seconds_all": [round(t, 3) for t in times],
+            "sample": f"first {tokens} of {w.N} tokens ({tokens / w.N:.1%}) of {w.name}: oracle routing (double "
+                      f"logits, float32 selection) + per-expert loop form in double; median of {runs} runs; "
+                      f"weight generation not timed"}
 
 
 def main():
@@ -357,7 +411,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=100)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=2048)
+    ap.add_argument("--cpu-tokens", type=int, default=1024)
+    ap.add_argument("--cpu-runs", type=int, default=3)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling rocprofv3 byte counters)")
     ap.add_argument("--profile-summary", metavar="DIR",
@@ -441,7 +496,7 @@ def main():
 
     if not args.no_cpu:
         print(f"[bench] cpu baseline: oracle on {args.cpu_tokens} tokens", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_tokens)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_tokens, args.cpu_runs)
     print(json.dumps(out), flush=True)
 
 

@@ -31,7 +31,8 @@
  *  - Errors: configuration and argument errors are detected on the host before
  *    anything is launched and returned as a status; a failed launch returns
  *    MOE_ERR_HIP. No exception crosses the ABI.
- *  - N = 0 is valid and launches nothing.
+ *  - N = 0 is valid and launches nothing (moe_dispatch: one small kernel that zeroes counts and
+ *    offsets).
  *  - Inputs must be finite. Router weight, bias, scores and mixture weights are
  *    float32 whatever `dtype` says; indices are int32.
  *  - Readings where the pages are open: discarded groups are excluded from the
@@ -96,25 +97,49 @@ typedef struct {
   const void* sh_gate;   /* [d_sh, D]; NULL iff n_shared_experts == 0 */
   const void* sh_up;     /* [d_sh, D] */
   const void* sh_down;   /* [D, d_sh] */
+  /* NULL, or moe_router_prepare's output for w_router (bf16 layers): the forward then reads it and skips
+   * splitting w_router on every call; w_router is not read and may be NULL. */
+  const void* w_router_prepared;
 } moe_weights;
 
-/* moe_route flag: read the float32 scores s [N, E] from `scores` and skip the gate GEMM. */
-#define MOE_ROUTE_SCORES_IN 1u
+/* moe_route flags. */
+#define MOE_ROUTE_SCORES_IN 1u  /* read the float32 scores s [N, E] from `scores`; skip the gate GEMM */
+#define MOE_ROUTE_SCORES_OUT 2u /* also write s [N, E] to `scores` (without it `scores` may be NULL) */
+#define MOE_ROUTE_PREPARED 4u   /* `w_router` is moe_router_prepare's output, not the float32 weight */
 
 /* Host only. MOE_OK if the config is valid and these kernels support it; otherwise
  * MOE_ERR_INVALID_ARG (not a valid layer) or MOE_ERR_UNSUPPORTED (outside the limits above). */
 moe_status moe_check_config(const moe_config* cfg);
 
-/* Host only. Bytes of workspace moe_forward and moe_dispatch need for N tokens (0 for an invalid
- * config): the most any batch of at most N tokens needs, so the size never falls as N grows and a
- * workspace sized for the largest batch serves every smaller one. */
+/* Host only. Bytes of workspace moe_forward, moe_forward_routed and moe_route need for N tokens (0 for
+ * an invalid config): the most any batch of at most N tokens needs, so the size never falls as N grows
+ * and a workspace sized for the largest batch serves every smaller one. */
 size_t moe_workspace_size(const moe_config* cfg, int64_t N);
+
+/* Host only. Bytes of workspace moe_dispatch needs for N tokens: per-chunk counts for batches of more
+ * than 256 tokens, 0 below (one kernel, no scratch). Never falls as N grows. */
+size_t moe_dispatch_workspace_size(const moe_config* cfg, int64_t N);
+
+/* Host only. Bytes of the prepared router weight of a bf16 layer: 3 * E * D * 2 (0 for float32 layers,
+ * which use w_router as given, or an invalid config). */
+size_t moe_router_prepared_size(const moe_config* cfg);
+
+/* Prepare the router weight of a bf16 layer once, for calls that would otherwise split it every time
+ * ("Group Router", How it works: the gate is evaluated in float32; the bf16 gate GEMM runs it as three
+ * exact bf16 pieces). prepared [3, E, D] bf16 (caller-owned, >= moe_router_prepared_size bytes) receives
+ * hi, mid and lo with hi + mid + lo == w_router exactly, each the bf16 rounding of what the pieces before
+ * it leave. Pass it as moe_weights.w_router_prepared or to moe_route with MOE_ROUTE_PREPARED; run it
+ * again whenever w_router changes. MOE_ERR_INVALID_ARG for float32 layers. Asynchronous on `stream`. */
+moe_status moe_router_prepare(const moe_config* cfg, const float* w_router, void* prepared, size_t bytes,
+                              void* stream);
 
 /* Router: gate GEMM + sigmoid, then group-restricted top-k and mixture weights ("Group Router").
  *   x        [N, D] of cfg->dtype (ignored with MOE_ROUTE_SCORES_IN)
- *   w_router [E, D] float32 (ignored with MOE_ROUTE_SCORES_IN)
+ *   w_router [E, D] float32, or with MOE_ROUTE_PREPARED the [3, E, D] bf16 output of moe_router_prepare
+ *            (ignored with MOE_ROUTE_SCORES_IN)
  *   e_bias   [E] float32
- *   scores   [N, E] float32: written with s (default) or read (MOE_ROUTE_SCORES_IN)
+ *   scores   [N, E] float32: read (MOE_ROUTE_SCORES_IN), written (MOE_ROUTE_SCORES_OUT), or unused and
+ *            may be NULL (neither flag). SCORES_IN excludes the other two flags.
  *   topk_idx [N, k] int32 out: the chosen experts in slot order
  *   topk_w   [N, k] float32 out: their weights, alpha included (unless alpha_on_output)
  *   workspace, ws_bytes: scratch of at least moe_workspace_size(cfg, N) bytes (unused, may be NULL,
@@ -123,7 +148,7 @@ size_t moe_workspace_size(const moe_config* cfg, int64_t N);
  * bf16 split of w_router, accumulated in float32 on the matrix cores). Given the same float32 scores,
  * indices and weights are bit-identical to a float32 evaluation in the order stated above (correctly
  * rounded add, divide and multiply). */
-moe_status moe_route(const moe_config* cfg, int64_t N, const void* x, const float* w_router, const float* e_bias,
+moe_status moe_route(const moe_config* cfg, int64_t N, const void* x, const void* w_router, const float* e_bias,
                      float* scores, uint32_t flags, int32_t* topk_idx, float* topk_w, void* workspace,
                      size_t ws_bytes, void* stream);
 
@@ -132,8 +157,11 @@ moe_status moe_route(const moe_config* cfg, int64_t N, const void* x, const floa
  *   topk_idx    [N, k] int32 in: expert ids in [0, E); E marks an empty slot
  *   counts      [E] int32 out: (token, slot) pairs per expert
  *   offsets     [E + 1] int32 out: exclusive scan of counts; offsets[E] = N * k less the empty slots
- *   sorted_pair [N * k] int32 out: the flat pair index n * k + slot at each expert-sorted position
+ *   sorted_pair [N * k] int32 out: the flat pair index n * k + slot at each expert-sorted position; the
+ *               token is sorted_pair / k (the page's per-expert token index list) and the slot, which
+ *               selects the mixture weight, is sorted_pair % k
  *   inv_row     [N * k] int32 out: the position of each pair (inverse of sorted_pair)
+ *   workspace, ws_bytes: at least moe_dispatch_workspace_size(cfg, N) bytes (may be NULL when that is 0)
  * Pairs whose id is outside [0, E) are left out of the lists (inv_row = -1); the lists are then
  * shorter than N * k and offsets[E] says so. */
 moe_status moe_dispatch(const moe_config* cfg, int64_t N, const int32_t* topk_idx, int32_t* counts,
@@ -181,10 +209,13 @@ moe_status moe_dense_forward(int64_t N, int32_t D, int32_t dff, int32_t dtype, f
 const char* moe_status_str(moe_status status);
 
 /* Per-stage timing for measurement. moe_profile_begin() starts recording a HIP event pair, on the
- * stream each call is given, around every kernel moe_forward / moe_route / moe_dispatch launch;
- * moe_profile_end() waits for those events, writes the summed milliseconds and launch counts per stage
- * (up to n_stages entries, indexed as moe_stage_name lists them) and stops recording. Returns
- * MOE_ERR_HIP if event creation or timing fails. Not thread-safe; for measurement only. */
+ * stream each call is given, around every kernel that moe_forward / moe_route / moe_dispatch launch
+ * from the calling thread; moe_profile_end() waits for those events, writes the summed milliseconds and
+ * launch counts per stage (up to n_stages entries, indexed as moe_stage_name lists them) and stops
+ * recording. The recording state is per thread: calls made by other threads are not recorded, and each
+ * thread's begin / end pair is independent. A thread's HIP events are reused across its recordings and
+ * live until the process ends. Returns MOE_ERR_HIP if event creation or timing fails. For measurement
+ * only: recording adds two event records around every launch. */
 moe_status moe_profile_begin(void);
 /* As moe_profile_begin, recording only the stages whose bit (1 << stage) is set in stage_mask (fewer
  * events in the stream when only some kernels are to be timed). */

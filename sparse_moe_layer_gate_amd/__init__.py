@@ -16,11 +16,12 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
-MOE_ROUTE_SCORES_IN = 1
+MOE_ROUTE_SCORES_IN, MOE_ROUTE_SCORES_OUT, MOE_ROUTE_PREPARED = 1, 2, 4
 
-EXPORTED = ["moe_check_config", "moe_workspace_size", "moe_route", "moe_dispatch", "moe_forward",
-            "moe_forward_routed", "moe_dense_workspace_size", "moe_dense_forward", "moe_status_str",
-            "moe_profile_begin", "moe_profile_begin_mask", "moe_profile_end", "moe_stage_name", "moe_stage_count"]
+EXPORTED = ["moe_check_config", "moe_workspace_size", "moe_dispatch_workspace_size", "moe_router_prepared_size",
+            "moe_router_prepare", "moe_route", "moe_dispatch", "moe_forward", "moe_forward_routed",
+            "moe_dense_workspace_size", "moe_dense_forward", "moe_status_str", "moe_profile_begin",
+            "moe_profile_begin_mask", "moe_profile_end", "moe_stage_name", "moe_stage_count"]
 
 
 class MoeError(RuntimeError):
@@ -48,7 +49,8 @@ class MoeConfig(ctypes.Structure):
 
 
 class MoeWeights(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in ("w_router", "e_bias", "gate_up", "down", "sh_gate", "sh_up", "sh_down")]
+    _fields_ = [(n, ctypes.c_void_p) for n in ("w_router", "e_bias", "gate_up", "down", "sh_gate", "sh_up", "sh_down",
+                                               "w_router_prepared")]
 
 
 _lib = None
@@ -67,6 +69,12 @@ def lib():
         L.moe_check_config.restype = ctypes.c_int
         L.moe_workspace_size.argtypes = [cp, i64]
         L.moe_workspace_size.restype = ctypes.c_size_t
+        L.moe_dispatch_workspace_size.argtypes = [cp, i64]
+        L.moe_dispatch_workspace_size.restype = ctypes.c_size_t
+        L.moe_router_prepared_size.argtypes = [cp]
+        L.moe_router_prepared_size.restype = ctypes.c_size_t
+        L.moe_router_prepare.argtypes = [cp, vp, vp, ctypes.c_size_t, vp]
+        L.moe_router_prepare.restype = ctypes.c_int
         L.moe_route.argtypes = [cp, i64, vp, vp, vp, vp, u32, vp, vp, vp, ctypes.c_size_t, vp]
         L.moe_route.restype = ctypes.c_int
         L.moe_dispatch.argtypes = [cp, i64, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
@@ -169,20 +177,48 @@ def alloc_workspace(cfg: MoeConfig, N: int, device="cuda"):
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
+def moe_dispatch_workspace_size(cfg: MoeConfig, N: int) -> int:
+    return int(lib().moe_dispatch_workspace_size(ctypes.byref(cfg), int(N)))
+
+
+def moe_router_prepared_size(cfg: MoeConfig) -> int:
+    return int(lib().moe_router_prepared_size(ctypes.byref(cfg)))
+
+
+def moe_router_prepare(cfg: MoeConfig, w_router, prepared=None, stream=None):
+    """The [3, E, D] bf16 pieces of w_router (bf16 layers), for moe_weights.w_router_prepared or moe_route
+    with MOE_ROUTE_PREPARED. Returns `prepared` (allocated here as a bf16 tensor when None)."""
+    import torch
+
+    E, D = cfg.n_routed_experts, cfg.hidden_size
+    if prepared is None:
+        prepared = torch.empty((3, E, D), dtype=torch.bfloat16, device=w_router.device)
+    st = lib().moe_router_prepare(ctypes.byref(cfg), _ptr(w_router, "w_router", torch.float32, (E, D)),
+                                  _ptr(prepared, "prepared"), prepared.numel() * prepared.element_size(),
+                                  _stream(stream))
+    _check(st, "moe_router_prepare")
+    return prepared
+
+
 def moe_route(cfg: MoeConfig, N: int, x, w_router, e_bias, scores, topk_idx, topk_w, flags: int = 0,
               workspace=None, stream=None):
     """Router on the GPU. With flags = MOE_ROUTE_SCORES_IN, `scores` [N, E] is read and x / w_router /
-    workspace are ignored; otherwise `workspace` (uint8, moe_workspace_size bytes) is required."""
+    workspace are ignored; otherwise `workspace` (uint8, moe_workspace_size bytes) is required, `scores`
+    is written with MOE_ROUTE_SCORES_OUT (else it may be None), and with MOE_ROUTE_PREPARED `w_router` is
+    the output of moe_router_prepare."""
     import torch
 
     E, D, k = cfg.n_routed_experts, cfg.hidden_size, cfg.num_experts_per_tok
     scores_in = bool(flags & MOE_ROUTE_SCORES_IN)
+    prepared = bool(flags & MOE_ROUTE_PREPARED)
+    need_scores = scores_in or bool(flags & MOE_ROUTE_SCORES_OUT)
     st = lib().moe_route(
         ctypes.byref(cfg), int(N),
         _ptr(x, "x", _act_dtype(cfg), (N, D), required=not scores_in),
-        _ptr(w_router, "w_router", torch.float32, (E, D), required=not scores_in),
+        _ptr(w_router, "w_router", torch.bfloat16 if prepared else torch.float32, (3, E, D) if prepared else (E, D),
+             required=not scores_in),
         _ptr(e_bias, "e_bias", torch.float32, (E,)),
-        _ptr(scores, "scores", torch.float32, (N, E)),
+        _ptr(scores, "scores", torch.float32, (N, E), required=need_scores),
         int(flags),
         _ptr(topk_idx, "topk_idx", torch.int32, (N, k)),
         _ptr(topk_w, "topk_w", torch.float32, (N, k)),
@@ -192,7 +228,10 @@ def moe_route(cfg: MoeConfig, N: int, x, w_router, e_bias, scores, topk_idx, top
     _check(st, "moe_route")
 
 
-def moe_dispatch(cfg: MoeConfig, N: int, topk_idx, counts, offsets, sorted_pair, inv_row, workspace, stream=None):
+def moe_dispatch(cfg: MoeConfig, N: int, topk_idx, counts, offsets, sorted_pair, inv_row, workspace=None,
+                 stream=None):
+    """Dispatch on the GPU; `workspace` (uint8, moe_dispatch_workspace_size bytes) may be None when that
+    size is 0."""
     import torch
 
     E, k = cfg.n_routed_experts, cfg.num_experts_per_tok
@@ -203,21 +242,22 @@ def moe_dispatch(cfg: MoeConfig, N: int, topk_idx, counts, offsets, sorted_pair,
         _ptr(offsets, "offsets", torch.int32, (E + 1,)),
         _ptr(sorted_pair, "sorted_pair", torch.int32, (N * k,)),
         _ptr(inv_row, "inv_row", torch.int32, (N * k,)),
-        _ptr(workspace, "workspace", torch.uint8),
-        workspace.numel(),
+        _ptr(workspace, "workspace", torch.uint8, required=False),
+        0 if workspace is None else workspace.numel(),
         _stream(stream))
     _check(st, "moe_dispatch")
 
 
 def weights_struct(cfg: MoeConfig, w: dict) -> MoeWeights:
-    """MoeWeights from a dict of device tensors: w_router, e_bias, gate_up, down, sh_gate, sh_up, sh_down
-    (the router pair may be absent for moe_forward_routed)."""
+    """MoeWeights from a dict of device tensors: w_router, e_bias, gate_up, down, sh_gate, sh_up, sh_down and
+    optionally w_router_prepared (the router pair may be absent for moe_forward_routed)."""
     import torch
 
     E, D, d = cfg.n_routed_experts, cfg.hidden_size, cfg.moe_intermediate_size
     dsh = d * cfg.n_shared_experts
     adt = _act_dtype(cfg)
     sh = cfg.n_shared_experts > 0
+    prep = w.get("w_router_prepared")
     return MoeWeights(
         _ptr(w.get("w_router"), "w_router", torch.float32, (E, D), required=False),
         _ptr(w.get("e_bias"), "e_bias", torch.float32, (E,), required=False),
@@ -226,6 +266,7 @@ def weights_struct(cfg: MoeConfig, w: dict) -> MoeWeights:
         _ptr(w.get("sh_gate"), "sh_gate", adt, (dsh, D), required=sh) if sh else None,
         _ptr(w.get("sh_up"), "sh_up", adt, (dsh, D), required=sh) if sh else None,
         _ptr(w.get("sh_down"), "sh_down", adt, (D, dsh), required=sh) if sh else None,
+        _ptr(prep, "w_router_prepared", torch.bfloat16, (3, E, D), required=False),
     )
 
 

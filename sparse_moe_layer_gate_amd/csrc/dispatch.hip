@@ -14,6 +14,7 @@ namespace {
 
 constexpr int CH = kDispatchChunk;
 constexpr int MAX_E = 512;
+constexpr int PL = 512, PW = PL / 64;  // threads (pairs per round) and waves of a placement block
 
 __global__ __launch_bounds__(256) void count_kernel(const int32_t* __restrict__ idx, int64_t N, int k, int E,
                                                     int32_t* __restrict__ chunk_counts) {
@@ -54,32 +55,12 @@ __device__ int block_exclusive_scan(int v, int* wsum, int* total) {
   return before + incl - v;
 }
 
-// Quotient of p / q for q > 0, in 32 bits when p fits (a 64-bit division is a long emulated sequence).
-__device__ inline uint64_t udiv(uint64_t p, uint32_t q) {
-  return p <= 0xffffffffull ? (uint64_t)((uint32_t)p / q) : p / q;
-}
-
-// Position in the merged list of the i-th small-expert tile (a) and of the j-th other tile (b), with na
-// and nb tiles in the two classes. The merge orders a tile by its fractional rank ((2 i + 1) / (2 na)
-// or (2 j + 1) / (2 nb); a before b on equal ranks), so every stretch of the list holds the two classes
-// in the same proportion. (a: the b tiles of smaller rank number ceil((2 i + 1) nb / na) / 2, rounded
-// down; b: the a tiles of rank at most its own number (floor((2 j + 1) na / nb) + 1) / 2.)
-__device__ inline int merged_pos_a(int i, int na, int nb) {
-  const uint64_t c = udiv((uint64_t)(2 * i + 1) * nb + na - 1, na);  // ceil
-  return i + (int)min((uint64_t)nb, c / 2);
-}
-__device__ inline int merged_pos_b(int j, int na, int nb) {
-  if (na == 0) return j;
-  const uint64_t f = udiv((uint64_t)(2 * j + 1) * na, nb);  // floor
-  return j + (int)min((uint64_t)na, (f + 1) / 2);
-}
-
 // Row-tile list of one grouped GEMM (called by every thread of the scan block; thread e < E holds
-// expert e's count and row offset). Order: the routed experts' tiles in expert order, then the shared
-// expert's, except that with ts.small_max > 0 the single tiles of experts with 1..small_max rows are
-// taken out and merged back evenly (merged_pos_*): the grouped kernels hand each XCD a contiguous run
-// of the list, and the merge gives every run the same mix of full tiles and nearly empty ones. An
-// expert's tiles stay together either way, so row tiles that share its weights still meet in one L2.
+// expert e's count and row offset). Order: the tiles of the routed experts in expert order, then the
+// shared expert's; with ts.small_max > 0 the single tiles of experts with 1..small_max rows (which
+// mostly stream their expert's weights) go after all of them. The persistent GEMM kernels balance the
+// XCDs by claiming work, and their rasterization rectangles then hold the full tiles of the large
+// experts, whose blocks run alike and share operands in L2, apart from the weight-streaming ones.
 __device__ void build_tiles(const TileSpec& ts, bool valid, int e, int cnt, int off, int64_t N,
                             int n_shared_problem, int* wsum) {
   const int nt = valid ? (cnt + ts.bm - 1) / ts.bm : 0;
@@ -90,14 +71,12 @@ __device__ void build_tiles(const TileSpec& ts, bool valid, int e, int cnt, int 
   const int nsh = n_shared_problem ? (int)((N + ts.bm - 1) / ts.bm) : 0;
   const int nb = nrouted + nsh;
   if (small) {
-    ts.tiles[merged_pos_a(ia, na, nb)] = Tile{0, e, off, cnt};
+    ts.tiles[nb + ia] = Tile{0, e, off, cnt};
   } else {
-    for (int j = 0; j < nt; ++j)
-      ts.tiles[merged_pos_b(ib + j, na, nb)] = Tile{0, e, off + j * ts.bm, min(ts.bm, cnt - j * ts.bm)};
+    for (int j = 0; j < nt; ++j) ts.tiles[ib + j] = Tile{0, e, off + j * ts.bm, min(ts.bm, cnt - j * ts.bm)};
   }
   for (int j = threadIdx.x; j < nsh; j += blockDim.x)
-    ts.tiles[merged_pos_b(nrouted + j, na, nb)] =
-        Tile{1, 0, j * ts.bm, (int)min((int64_t)ts.bm, N - (int64_t)j * ts.bm)};
+    ts.tiles[nrouted + j] = Tile{1, 0, j * ts.bm, (int)min((int64_t)ts.bm, N - (int64_t)j * ts.bm)};
   if (threadIdx.x == 0) *ts.n_tiles = na + nb;
   if (ts.work_ctr && threadIdx.x < 8) ts.work_ctr[threadIdx.x] = 0;
 }
@@ -141,8 +120,9 @@ __global__ __launch_bounds__(512) void scan_kernel(const int32_t* __restrict__ c
   }
   if (e == 0) offsets[E] = total;
   // the shared expert's tiles cover all N tokens, in token order
-  build_tiles(t0, e < E, e, cnt, off, N, n_shared_problem, wsum);
-  build_tiles(t1, e < E, e, cnt, off, N, n_shared_problem, wsum);
+  // (no lists when dispatch runs on its own: the tile pointers are null for every thread alike)
+  if (t0.tiles) build_tiles(t0, e < E, e, cnt, off, N, n_shared_problem, wsum);
+  if (t1.tiles) build_tiles(t1, e < E, e, cnt, off, N, n_shared_problem, wsum);
   // both lists built (t0 of 16-row tiles, t1 of 256-row tiles): empty the one whose kernels do not run
   // (thread 0 wrote both counts above)
   if (pick_rows > 0 && threadIdx.x == 0) *(max_cnt <= pick_rows ? t1.n_tiles : t0.n_tiles) = 0;
@@ -152,7 +132,6 @@ __global__ __launch_bounds__(512) void scan_kernel(const int32_t* __restrict__ c
 // position is its expert's running offset + the pairs of that expert in earlier waves of the round +
 // those in earlier lanes of its own wave (found with one ballot per bit of the expert id). Tokens stay
 // ascending inside each expert because pairs are visited in (token, slot) order.
-constexpr int PL = 512, PW = PL / 64;  // threads (pairs per round) and waves of a placement block
 
 __global__ __launch_bounds__(PL) void place_kernel(const int32_t* __restrict__ idx, int64_t N, int k, int E,
                                                     const int32_t* __restrict__ chunk_base,
@@ -207,6 +186,87 @@ __global__ __launch_bounds__(PL) void place_kernel(const int32_t* __restrict__ i
   }
 }
 
+// The whole dispatch of a batch of at most one chunk (N <= kDispatchChunk tokens) in one block: the
+// histogram, the scan and tile lists of scan_kernel, then the stable placement of place_kernel with the
+// expert offsets as the chunk's bases. Same results, bit for bit, as the three kernels; one launch
+// instead of three, which is most of the dispatch time of a decode step.
+__global__ __launch_bounds__(PL) void dispatch_small_kernel(const int32_t* __restrict__ idx, int64_t N, int k, int E,
+                                                            int n_shared_problem, int32_t* __restrict__ counts,
+                                                            int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ sorted_pair,
+                                                            int32_t* __restrict__ inv_row, TileSpec t0, TileSpec t1,
+                                                            int pick_rows) {
+  __shared__ int running[MAX_E];  // the histogram, then each expert's next free position
+  __shared__ int wcnt[PW][MAX_E];
+  __shared__ int wsum[8];
+  __shared__ int max_cnt;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int npairs = (int)(N * k);
+  for (int e = t; e < E; e += PL) {
+    running[e] = 0;
+    for (int w = 0; w < PW; ++w) wcnt[w][e] = 0;
+  }
+  if (t == 0) max_cnt = 0;
+  __syncthreads();
+  for (int p = t; p < npairs; p += PL) {
+    const int e = idx[p];
+    if (e >= 0 && e < E) atomicAdd(&running[e], 1);
+  }
+  __syncthreads();
+  const int e = t;  // E <= 512 = PL: one expert per thread
+  const int cnt = e < E ? running[e] : 0;
+  if (pick_rows > 0 && cnt > 0) atomicMax(&max_cnt, cnt);  // read after the scan's barriers
+  int total;
+  const int off = block_exclusive_scan(cnt, wsum, &total);
+  if (e < E) {
+    counts[e] = cnt;
+    offsets[e] = off;
+    running[e] = off;  // only thread e reads or writes entry e here; the barriers below publish it
+  }
+  if (e == 0) offsets[E] = total;
+  if (t0.tiles) build_tiles(t0, e < E, e, cnt, off, N, n_shared_problem, wsum);
+  if (t1.tiles) build_tiles(t1, e < E, e, cnt, off, N, n_shared_problem, wsum);
+  if (pick_rows > 0 && t == 0) *(max_cnt <= pick_rows ? t1.n_tiles : t0.n_tiles) = 0;
+  __syncthreads();
+  const int ebits = E > 1 ? 32 - __clz(E - 1) : 0;
+  for (int r0 = 0; r0 < npairs; r0 += PL) {
+    const int p = r0 + t;
+    int pe = -1;
+    if (p < npairs) {
+      pe = idx[p];
+      if (pe < 0 || pe >= E) {
+        pe = -1;
+        inv_row[p] = -1;
+      }
+    }
+    uint64_t same = __ballot(pe >= 0);
+    for (int b = 0; b < ebits; ++b) {
+      const bool bit = (pe >> b) & 1;
+      const uint64_t m = __ballot(bit);
+      same &= bit ? m : ~m;
+    }
+    const int rank = __popcll(same & ((1ull << lane) - 1));
+    if (pe >= 0 && rank == 0) wcnt[wave][pe] = __popcll(same);
+    __syncthreads();
+    if (pe >= 0) {
+      int pos = running[pe] + rank;
+      for (int w = 0; w < wave; ++w) pos += wcnt[w][pe];
+      sorted_pair[pos] = p;
+      inv_row[p] = pos;
+    }
+    __syncthreads();
+    for (int e2 = t; e2 < E; e2 += PL) {
+      int add = 0;
+      for (int w = 0; w < PW; ++w) {
+        add += wcnt[w][e2];
+        wcnt[w][e2] = 0;
+      }
+      running[e2] += add;
+    }
+    __syncthreads();
+  }
+}
+
 // Tile lists of one dense problem (problem 0, expert 0) over N rows, for the dense FFN.
 __global__ __launch_bounds__(256) void dense_tiles_kernel(int64_t N, TileSpec t0, TileSpec t1) {
   for (int which = 0; which < 2; ++which) {
@@ -230,6 +290,23 @@ __global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* __restrict__ p, 
 }
 
 }  // namespace
+
+__global__ __launch_bounds__(256) void fill2_i32_kernel(int32_t* __restrict__ p, int64_t n, int32_t* __restrict__ q,
+                                                       int64_t m, int32_t v) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n + m; i += (int64_t)gridDim.x * 256) {
+    if (i < n)
+      p[i] = v;
+    else
+      q[i - n] = v;
+  }
+}
+
+hipError_t launch_fill2_i32(int32_t* p, int64_t n, int32_t* q, int64_t m, int32_t v, hipStream_t s) {
+  if (n + m <= 0) return hipSuccess;
+  const int64_t blocks = min((n + m + 255) / 256, (int64_t)1024);
+  hipLaunchKernelGGL(fill2_i32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n, q, m, v);
+  return hipGetLastError();
+}
 
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s) {
   if (n <= 0) return hipSuccess;
@@ -256,6 +333,15 @@ hipError_t launch_scan(const int32_t* chunk_counts, int nchunks, int64_t N, int 
                        int pick_rows, hipStream_t s) {
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(512), 0, s, chunk_counts, nchunks, N, k, E, n_shared_problem, counts,
                      offsets, chunk_base, t0, t1, pick_rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch_small(const int32_t* idx, int64_t N, int k, int E, int n_shared_problem, int32_t* counts,
+                                 int32_t* offsets, int32_t* sorted_pair, int32_t* inv_row, TileSpec t0, TileSpec t1,
+                                 int pick_rows, hipStream_t s) {
+  if (N > CH) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(PL), 0, s, idx, N, k, E, n_shared_problem, counts, offsets,
+                     sorted_pair, inv_row, t0, t1, pick_rows);
   return hipGetLastError();
 }
 

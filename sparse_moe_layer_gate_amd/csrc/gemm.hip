@@ -182,15 +182,12 @@ int tile_plan_rows(int i) { return i == 0 ? MOE_DECODE_ROWS : MOE_PICK_BAND_ROWS
 #define MOE_SMALL_EXPERT_ROWS 128  // 256-row tiles: experts with at most half a tile of rows
 #endif
 
-// Tile order (see build_tiles): the grouped kernels give each XCD a contiguous run of the tile list,
-// and in expert order the runs can hold very different work: under skewed routing a run that draws
-// several hot experts' full tiles takes far longer than one of nearly empty single-tile experts, whose
-// blocks mostly stream weights. Spreading the tiles of experts with at most half a tile of rows evenly
-// over the list evens the runs out. Measured on the two GEMMs (gate_up / down ms, expert order ->
-// spread): skewed GLM-4.5 layer 2.74 / 1.47 -> 2.57 / 1.39, GLM-5 prefill 4.51 / 2.38 -> 4.46 / 2.36,
-// 288-expert prefill 3.21 / 1.66 -> 3.19 / 1.63, Air 1.07 / 0.57 -> 1.06 / 0.56. Spreading single tiles
-// (a hot expert's partial last tile apart from its full ones) instead of whole experts loses on GLM-5,
-// where it separates row tiles that share an expert's weights.
+// Tile order (see build_tiles): the single tiles of experts with at most half a tile of rows, which
+// mostly stream their expert's weights, go after the other tiles, so that the rasterization rectangles
+// of the prefill kernels hold the large experts' tiles together. (An earlier order merged them evenly
+// among the others to balance the XCDs' runs before the kernels claimed work per XCD; with the claiming
+// kernels and 2 x 16 rectangles the separated order is 2-4% faster on GLM-5 and Air and equal on the
+// skewed GLM-4.5 layer.)
 int small_expert_rows(int dtype, int bm) { return (dtype == MOE_BF16 && bm == 256) ? MOE_SMALL_EXPERT_ROWS : 0; }
 
 hipError_t launch_gate_up(int dtype, const GroupedArgs& a, int64_t max_tile_count, hipStream_t s) {

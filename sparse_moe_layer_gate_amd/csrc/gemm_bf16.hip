@@ -2,20 +2,19 @@
 //
 // Same products as the generic grouped kernels ("MoE Forward", eq. E_i: the gate_up GEMM with the
 // SwiGLU applied in registers, and the down GEMM scaled by the mixture weight w_{n,i}), laid out for
-// gfx950. Two kernels:
-//  - grouped_bf16_w8 (the one the forward runs): eight waves, two per SIMD, each wave computing a
-//    64 x 128 share of a 256 x 256 tile and issuing an eighth of every step's loads (described where
-//    it is defined); persistent, one block per CU claiming tiles per XCD;
-//  - grouped_bf16_lds (fallback when x spans 4 GiB or more, where the eight-wave kernel's 32-bit
-//    buffer offsets do not reach): four waves, each 128 x 128 of the tile.
-// Common to both:
+// gfx950: grouped_bf16_w8, eight waves, two per SIMD, each wave computing a 64 x 128 share of a
+// 256 x 256 tile and issuing an eighth of every step's loads (described where it is defined);
+// persistent, one block per CU claiming tiles per XCD.
 //  - operands go global -> LDS directly (lane l of a wave writes bytes [16 l, 16 l + 16) of a 1 KiB
 //    run), no register staging;
-//  - LDS rows are BK bf16 long, unpadded; the 16-byte chunks of a row are XOR-swizzled by the row's
+//  - LDS rows are 64 bf16 long, unpadded; the 16-byte chunks of a row are XOR-swizzled by the row's
 //    position so that the MFMA operand reads (32 rows at one k offset) hit distinct banks;
 //  - v_mfma_f32_32x32x16_bf16 tiles; 32-row MFMA sub-tiles past a tile's valid rows are skipped, so a
 //    sparsely filled tile (a rarely chosen expert) costs little MFMA time;
-//  - blocks follow an XCD-aware order over the valid tiles with a row-tile-major rasterization.
+//  - blocks follow an XCD-aware order over the valid tiles, rasterized in rectangles of row tiles x
+//    column tiles so that the blocks one XCD runs together share both operands in its L2.
+//  - operands are addressed with 32-bit byte offsets from x (gathered rows), from a tile's first row,
+//    or from an expert's matrix; the host rejects layers whose x or expert matrices reach 4 GiB.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -25,339 +24,24 @@
 namespace moe {
 namespace {
 
-// Rasterization: row tiles per column sweep (see grouped_bf16_lds), for gate_up and down.
+// Rasterization rectangles (see w8_block): row tiles x column tiles, for gate_up and down. Measured
+// (layer ms; 1-D groups of 32 / 16 row tiles down whole columns -> 2 x 16 rectangles, with the small
+// experts' tiles after the others, see build_tiles): GLM-5 prefill 6.95 -> 6.77, Air 1.71 -> 1.65,
+// skewed GLM-4.5 4.17 -> 4.16; 8 x 4, 4 x 12 and 16 x 2 rectangles were within 1% of 2 x 16 or slower.
 #ifndef MOE_PF_GROUP_ROWS_GU
-#define MOE_PF_GROUP_ROWS_GU 32
+#define MOE_PF_GROUP_ROWS_GU 2
+#endif
+#ifndef MOE_PF_GROUP_COLS_GU
+#define MOE_PF_GROUP_COLS_GU 16
 #endif
 #ifndef MOE_PF_GROUP_ROWS_DN
-#define MOE_PF_GROUP_ROWS_DN 16
+#define MOE_PF_GROUP_ROWS_DN 2
 #endif
-// L2 line touches ahead of the ring (see PrefillTile::TOUCH): distance in K steps (0: off) for the
-// gate_up and down GEMMs, the smallest routed-expert row count that turns them on, and which operands
-// (bit 0: A, bit 1: B) are touched.
-#ifndef MOE_PF_TOUCH_GU
-#define MOE_PF_TOUCH_GU 0
+#ifndef MOE_PF_GROUP_COLS_DN
+#define MOE_PF_GROUP_COLS_DN 16
 #endif
-#ifndef MOE_PF_TOUCH_DN
-#define MOE_PF_TOUCH_DN 2
-#endif
-#ifndef MOE_PF_TOUCH_MIN_ROWS
-#define MOE_PF_TOUCH_MIN_ROWS 1024
-#endif
-#ifndef MOE_PF_TOUCH_GU_OPS
-#define MOE_PF_TOUCH_GU_OPS 3
-#endif
-#ifndef MOE_PF_TOUCH_DN_OPS
-#define MOE_PF_TOUCH_DN_OPS 1
-#endif
-
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-template <int V>
-struct IntC {
-  static constexpr int value = V;
-};
-template <bool V>
-struct BoolC {
-  static constexpr bool value = V;
-};
-
-template <int BM, int BK, int STAGES, bool GATE_UP>
-struct PrefillTile {
-  static constexpr int BN = 256;
-  static constexpr int WM = BM == 256 ? 2 : 1, WN = 4 / WM;
-  static constexpr int WAVE_M = BM / WM, WAVE_N = BN / WN;
-  static constexpr int TM = WAVE_M / 32, TN = WAVE_N / 32;
-  static constexpr int ROWB = BK * 2;        // bytes per LDS row
-  static constexpr int CPR = BK / 8;         // 16-byte chunks per row
-  static constexpr int NA = BM * CPR / 256;  // direct loads per thread per K step (A)
-  static constexpr int NB = BN * CPR / 256;  // (B)
-  static constexpr int LPS = NA + NB;
-  static constexpr int STAGE_BYTES = (BM + BN) * ROWB;
-  static constexpr int COLS = GATE_UP ? BN / 2 : BN;  // output columns per block
-  static_assert(TN % 2 == 0, "gate_up pairs gate and up column tiles inside a wave");
-  static_assert(CPR == 8 || CPR == 4, "BK is 64 or 32");
-  // L2 warm-up: with a two-stage ring a step's operands have one step of compute to arrive, less
-  // than a miss to HBM takes. For tiles of large experts (whose B is shared by many row tiles and stays
-  // cached, so the A rows are what misses) each lane also touches one line of the selected operands
-  // TOUCH steps ahead (4-byte direct loads into a scratch word), so the later full loads hit L2.
-  // Measured: it pays for down on row-heavy experts; elsewhere the extra requests cost more.
-  static constexpr int TOUCH = STAGES == 2 ? (GATE_UP ? MOE_PF_TOUCH_GU : MOE_PF_TOUCH_DN) : 0;
-  static constexpr int TOUCH_OPS = GATE_UP ? MOE_PF_TOUCH_GU_OPS : MOE_PF_TOUCH_DN_OPS;  // bit 0: A, bit 1: B
-  static constexpr int NTOUCH = (TOUCH_OPS & 1) + ((TOUCH_OPS >> 1) & 1);
-
-  // Chunk swizzle: the 16-byte chunk c of LDS row r is stored in slot c ^ swz(r). swz depends on
-  // r mod 32 only, and any 8 (and any aligned 16) consecutive rows get distinct slots, so the MFMA
-  // operand reads (32 rows x one chunk) are free of bank conflicts for 8- or 16-lane LDS passes.
-  __device__ static int swz(int r) {
-    r &= 31;
-    if (CPR == 8) return (r ^ (r >> 3)) & 7;
-    return ((r >> 1) ^ (r >> 3)) & 3;
-  }
-
-  // One K step's direct loads: load q of wave w fills the operand's chunks [(4 q + w) 64, + 64).
-  __device__ static void issue(char* lds, const uint16_t* const (&srcA)[NA], const uint16_t* const (&srcB)[NB],
-                               int kstep, int wave) {
-    char* st = lds + (kstep % STAGES) * STAGE_BYTES;
-    const int k0 = kstep * BK;
-#pragma unroll
-    for (int q = 0; q < NA; ++q)
-      if (srcA[q])  // rows past the tile's valid rows are not loaded (their MFMA outputs are not stored)
-        __builtin_amdgcn_global_load_lds((const void*)(srcA[q] + k0), (lds_void*)(st + (q * 4 + wave) * 1024), 16, 0,
-                                         0);
-#pragma unroll
-    for (int q = 0; q < NB; ++q)
-      __builtin_amdgcn_global_load_lds((const void*)(srcB[q] + k0), (lds_void*)(st + BM * ROWB + (q * 4 + wave) * 1024),
-                                       16, 0, 0);
-  }
-
-  __device__ static int b_row(int j, int wn) {
-    if (GATE_UP) return (j < TN / 2 ? 0 : BN / 2) + wn * (WAVE_N / 2) + (j % (TN / 2)) * 32;
-    return wn * WAVE_N + j * 32;
-  }
-
-  // The K loop for a wave whose first MI 32-row sub-tiles hold valid rows (MI = 0: loads only).
-  template <int MI, bool TOUCHING>
-  __device__ static __attribute__((always_inline)) void run(char* lds, const uint16_t* const (&srcA)[NA],
-                                                            const uint16_t* const (&srcB)[NB], f32x16 (&acc)[TM][TN],
-                                                            int nk, int wave, int lane, int wm, int wn,
-                                                            const uint16_t* touchA, const uint16_t* touchB,
-                                                            int* sink) {
-    auto touch = [&](int kstep) {
-      if (TOUCH_OPS & 1) __builtin_amdgcn_global_load_lds((const void*)(touchA + kstep * BK), (lds_void*)sink, 4, 0, 0);
-      if (TOUCH_OPS & 2) __builtin_amdgcn_global_load_lds((const void*)(touchB + kstep * BK), (lds_void*)sink, 4, 0, 0);
-    };
-    const int sw = swz(lane & 31);
-    const int a_off = (wm * WAVE_M + (lane & 31)) * ROWB;
-    int b_off[TN];
-#pragma unroll
-    for (int j = 0; j < TN; ++j) b_off[j] = BM * ROWB + (b_row(j, wn) + (lane & 31)) * ROWB;
-#pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s)
-      if (s < nk) issue(lds, srcA, srcB, s, wave);
-    if (TOUCHING && TOUCH < nk) touch(TOUCH);
-    for (int kt = 0; kt < nk; ++kt) {
-      // Step kt's direct loads are this wave's oldest outstanding VMEM ops (only the two touches of
-      // step kt + TOUCH, issued right after them, may be newer); once every wave has waited for its
-      // own and met at the barrier, step kt is in LDS. The barrier also ends every wave's reads of the
-      // stage that the next issue() refills (they fed MFMAs of step kt - 1). A plain s_barrier:
-      // __syncthreads() would add a vmcnt(0) wait and drain the prefetches of later steps.
-      if (TOUCHING && kt + TOUCH < nk)
-        wait_vmcnt<NTOUCH>();
-      else if (kt + STAGES - 2 < nk)
-        wait_vmcnt<(STAGES - 2) * LPS>();
-      else
-        wait_vmcnt<0>();
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      __builtin_amdgcn_s_barrier();
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      if (kt + STAGES - 1 < nk) {
-        issue(lds, srcA, srcB, kt + STAGES - 1, wave);
-        if (TOUCHING && kt + 1 + TOUCH < nk) touch(kt + 1 + TOUCH);
-      }
-      if (MI == 0) continue;
-      const char* st = lds + (kt % STAGES) * STAGE_BYTES;
-      bf16x8 af[2][MI > 0 ? MI : 1], bfr[2][TN];
-      auto load_frags = [&](int kk, int buf) {
-        const int coff = ((2 * kk + (lane >> 5)) ^ sw) * 16;
-#pragma unroll
-        for (int j = 0; j < TN; ++j) bfr[buf][j] = *(const bf16x8*)(st + b_off[j] + coff);
-#pragma unroll
-        for (int i = 0; i < MI; ++i) af[buf][i] = *(const bf16x8*)(st + a_off + i * 32 * ROWB + coff);
-      };
-      load_frags(0, 0);
-#pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        if (kk + 1 < BK / 16) load_frags(kk + 1, (kk + 1) & 1);
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk & 1][i], bfr[kk & 1][j], acc[i][j], 0, 0, 0);
-      }
-      schedule<MI>();
-    }
-  }
-
-  // Instruction order of one K step: the first slice's operand reads, then each slice's MFMAs with the
-  // next slice's reads spread between them, so LDS latency hides under MFMA work.
-  template <int MI>
-  __device__ static __attribute__((always_inline)) void schedule() {
-#ifndef MOE_PF_NO_SCHED
-    constexpr int R = MI + TN;   // LDS reads per slice
-    constexpr int M = MI * TN;   // MFMAs per slice
-    constexpr int PER = M / R > 0 ? M / R : 1;
-    __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
-#pragma unroll
-    for (int kk = 0; kk + 1 < BK / 16; ++kk) {
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      if (M > PER * R) __builtin_amdgcn_sched_group_barrier(0x008, M - PER * R, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, M, 0);
-#endif
-  }
-};
-
-template <int BM, int BK, int STAGES, bool GATE_UP>
-__global__ __launch_bounds__(256, 1) void grouped_bf16_lds(GroupedArgs a, int ncol_max) {
-  using T = PrefillTile<BM, BK, STAGES, GATE_UP>;
-  constexpr int BN = T::BN, CPR = T::CPR, NA = T::NA, NB = T::NB, TM = T::TM, TN = T::TN;
-  constexpr int WAVE_M = T::WAVE_M, WAVE_N = T::WAVE_N;
-
-  constexpr int OUT_BYTES = 4 * WAVE_M * ((GATE_UP ? WAVE_N / 2 : WAVE_N) + 8) * 2;
-  constexpr int LDS_BYTES = STAGES * T::STAGE_BYTES > OUT_BYTES ? STAGES * T::STAGE_BYTES : OUT_BYTES;
-  __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
-  __shared__ float wrow[BM];
-  __shared__ int touch_sink[64];
-
-  // Rasterization: logical ids walk GR row tiles down a column before moving right, so the blocks
-  // one XCD runs together share GR-fold the B slices and (32 / GR)-fold the A slices.
-  const int64_t n_tiles = *a.n_tiles;
-  const int64_t L = xcd_logical_block(n_tiles * ncol_max);
-  if (L < 0) return;
-  constexpr int GR = GATE_UP ? MOE_PF_GROUP_ROWS_GU : MOE_PF_GROUP_ROWS_DN;
-  const int64_t sg = L / ((int64_t)GR * ncol_max), within = L % ((int64_t)GR * ncol_max);
-  // the last group may hold fewer than GR row tiles
-  const int64_t gr = min((int64_t)GR, n_tiles - sg * GR);
-  const int64_t tile_id = sg * GR + within % gr;
-  const int ct = (int)(within / gr);
-  const Tile tile = a.tiles[tile_id];
-  const ExpertProblem P = pick_problem(a, tile.problem);
-  const int col0 = ct * T::COLS;
-  if (col0 >= P.ncols) return;
-
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int wm = wave / T::WN, wn = wave % T::WN;
-
-  // Global source of each direct load: LDS chunk p is row p / CPR, slot p % CPR, which holds the
-  // row's logical chunk slot ^ swz(row).
-  const uint16_t* srcA[NA];
-  const uint16_t* srcB[NB];
-#pragma unroll
-  for (int q = 0; q < NA; ++q) {
-    const int p = (q * 4 + wave) * 64 + lane;
-    const int r = p / CPR, c = (p % CPR) ^ T::swz(r);
-    int64_t g = (int64_t)tile.row_start + min(r, tile.rows - 1);
-    if (P.gather) g = a.sorted_pair[g] / a.k;
-    srcA[q] = (const uint16_t*)P.A + g * P.lda + 8 * c;
-    // Skipping a load leaves fewer VMEM ops in flight than the vmcnt thresholds of a deeper ring
-    // assume, so only the two-stage ring (which waits for all of them) skips.
-    if (STAGES == 2 && r >= tile.rows) srcA[q] = nullptr;
-  }
-#pragma unroll
-  for (int q = 0; q < NB; ++q) {
-    const int p = (q * 4 + wave) * 64 + lane;
-    const int r = p / CPR, c = (p % CPR) ^ T::swz(r);
-    const uint16_t* base;
-    int col;
-    if (GATE_UP) {
-      base = (const uint16_t*)(r < BN / 2 ? P.B0 : P.B1);
-      col = min(col0 + (r % (BN / 2)), P.ncols - 1);
-    } else {
-      base = (const uint16_t*)P.B0;
-      col = min(col0 + r, P.ncols - 1);
-    }
-    srcB[q] = base + (int64_t)tile.expert * P.b_stride + (int64_t)col * P.K + 8 * c;
-  }
-  // The shared expert's down GEMM (every token) counts as large.
-  const bool touch_on = T::TOUCH > 0 && (tile.problem == 1 || !a.offsets ||
-                                         a.offsets[tile.expert + 1] - a.offsets[tile.expert] >= MOE_PF_TOUCH_MIN_ROWS);
-  // Line-touch sources: A row t (clamped to the tile) and B row t, at chunk 0.
-  const uint16_t* touchA;
-  const uint16_t* touchB;
-  {
-    int64_t g = (int64_t)tile.row_start + min(t, tile.rows - 1);
-    if (P.gather) g = a.sorted_pair[g] / a.k;
-    touchA = (const uint16_t*)P.A + g * P.lda;
-    const uint16_t* base;
-    int col;
-    if (GATE_UP) {
-      base = (const uint16_t*)(t % BN < BN / 2 ? P.B0 : P.B1);
-      col = min(col0 + t % (BN / 2), P.ncols - 1);
-    } else {
-      base = (const uint16_t*)P.B0;
-      col = min(col0 + t % BN, P.ncols - 1);
-    }
-    touchB = base + (int64_t)tile.expert * P.b_stride + (int64_t)col * P.K;
-  }
-  if (!GATE_UP && t < BM) {
-    const int r = min(t, tile.rows - 1);
-    wrow[t] = P.scale_rows ? a.topk_w[a.sorted_pair[tile.row_start + r]] : 1.0f;
-  }
-
-  f32x16 acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  const int nk = P.K / BK;
-  const int live_m = tile.rows - wm * WAVE_M;  // valid rows of this wave's slab
-  const int mi = live_m <= 0 ? 0 : min(TM, (live_m + 31) / 32);
-  auto run = [&](auto mi_tag, auto touch_tag) {
-    T::template run<decltype(mi_tag)::value, decltype(touch_tag)::value>(lds, srcA, srcB, acc, nk, wave, lane, wm, wn,
-                                                                         touchA, touchB, touch_sink);
-  };
-  auto run_mi = [&](auto touch_tag) {
-    switch (mi) {
-      case 0: run(IntC<0>{}, touch_tag); break;
-      case 1: run(IntC<1>{}, touch_tag); break;
-      case 2: run(IntC<(TM >= 2 ? 2 : 1)>{}, touch_tag); break;
-      case 3: run(IntC<(TM >= 3 ? 3 : 1)>{}, touch_tag); break;
-      default: run(IntC<TM>{}, touch_tag); break;
-    }
-  };
-  if (T::TOUCH > 0 && touch_on)
-    run_mi(BoolC<true>{});
-  else
-    run_mi(BoolC<false>{});
-
-  // Epilogue through LDS: each wave writes its bf16 results (SwiGLU / weight scale applied) into its
-  // own padded region, then stores whole 16-byte row chunks, so a store instruction covers
-  // contiguous runs of the output rows instead of 2-byte scatters.
-  constexpr int OC = GATE_UP ? WAVE_N / 2 : WAVE_N;  // output columns per wave
-  constexpr int OPITCH = OC + 8;                      // bf16 per staged row (16-byte pad: the two
-                                                      // half-waves' rows land on disjoint banks)
-  __syncthreads();  // every wave is done reading the operand ring
-  uint16_t* stage_out = (uint16_t*)lds + wave * (WAVE_M * OPITCH);
-  // 32x32 C layout: lane holds column lane % 32, rows 8 (r / 4) + 4 (lane / 32) + r % 4.
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    if (i >= mi) continue;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);  // within the wave slab
-      if (GATE_UP) {
-#pragma unroll
-        for (int j = 0; j < TN / 2; ++j)
-          stage_out[row * OPITCH + j * 32 + (lane & 31)] = bf16_rne(swiglu_bf16(acc[i][j][r], acc[i][j + TN / 2][r], a.swiglu_limit));
-      } else {
-        const float sc = wrow[min(wm * WAVE_M + row, BM - 1)];
-#pragma unroll
-        for (int j = 0; j < TN; ++j) stage_out[row * OPITCH + j * 32 + (lane & 31)] = bf16_rne(acc[i][j][r] * sc);
-      }
-    }
-  }
-  __syncthreads();
-  uint16_t* out = (uint16_t*)P.out;
-  const int ocol0 = col0 + wn * OC;
-  constexpr int CH = OC / 8;  // 16-byte chunks per staged row
-  const int rows_here = min(WAVE_M, tile.rows - wm * WAVE_M);
-  for (int c = lane; c < rows_here * CH; c += 64) {
-    const int row = c / CH, ch = c % CH;
-    const int col = ocol0 + ch * 8;
-    if (col < P.ncols) {  // ncols is a multiple of 64: a chunk is wholly in or out
-      const uint4 v = *(const uint4*)(stage_out + row * OPITCH + ch * 8);
-      *(uint4*)(out + ((int64_t)tile.row_start + wm * WAVE_M + row) * P.ldo + col) = v;
-    }
-  }
-}
 
 // ---- eight-wave kernel for 256-row tiles ----
 //
@@ -368,7 +52,7 @@ __global__ __launch_bounds__(256, 1) void grouped_bf16_lds(GroupedArgs a, int nc
 // each with its own 64 x 128 share of the tile, its own fragment reads and an eighth of every step's
 // loads: while one of them waits on the load path, the other keeps the matrix core busy.
 //  - block tile 256 x 256, BK = 64 (whole 128-byte lines per row and load); A in a two-stage ring, B
-//    in a three-stage ring, together all 160 KiB of LDS; rows chunk-swizzled as in PrefillTile;
+//    in a three-stage ring, together all 160 KiB of LDS; rows chunk-swizzled (Wave8Tile::swz);
 //  - half g = w / 4 owns tile rows [128 g, 128 g + 128); wave w % 4 = 2 wn + mh owns 64 rows (mh) of
 //    that half and 128 B rows (wn), as 2 x 4 tiles of v_mfma_f32_32x32x16_bf16 (gate_up: 64 gate rows
 //    and the matching 64 up rows, so SwiGLU pairs stay in one wave);
@@ -614,11 +298,17 @@ __device__ __forceinline__ void w8_block(const GroupedArgs& a, int ncol_max, int
   constexpr int WROW_OFF = OUT_BYTES;  // row scales (down), after the staged outputs
   static_assert(T::RING <= 160 * 1024 && WROW_OFF + 256 * 4 <= T::RING, "LDS budget");
 
+  // Rasterization: logical ids walk rectangles of GR row tiles x GC column tiles (the last ones of a
+  // row group or of the tile list smaller), row tiles fastest. The blocks an XCD runs at one time are
+  // consecutive logical ids, so they cover about one rectangle and read GR A slices and GC B slices
+  // per K step between them instead of one of each per block.
   constexpr int GR = GATE_UP ? MOE_PF_GROUP_ROWS_GU : MOE_PF_GROUP_ROWS_DN;
+  constexpr int GC = GATE_UP ? MOE_PF_GROUP_COLS_GU : MOE_PF_GROUP_COLS_DN;
   const int64_t sg = L / ((int64_t)GR * ncol_max), within = L % ((int64_t)GR * ncol_max);
   const int64_t gr = min((int64_t)GR, n_tiles - sg * GR);
-  const int64_t tile_id = sg * GR + within % gr;
-  const int ct = (int)(within / gr);
+  const int64_t cg = within / (gr * GC), w2 = within % (gr * GC);
+  const int64_t tile_id = sg * GR + w2 % gr;
+  const int ct = (int)(cg * GC + w2 / gr);
   const Tile tile = a.tiles[tile_id];
   const ExpertProblem P = pick_problem(a, tile.problem);
   const int col0 = ct * T::COLS;
@@ -767,20 +457,11 @@ __global__ __launch_bounds__(512, 1) void grouped_bf16_w8(GroupedArgs a, int nco
   }
 }
 
-#ifndef MOE_PF_EIGHT_WAVES
-#define MOE_PF_EIGHT_WAVES 1
-#endif
-
-#ifndef MOE_PF_BK
-#define MOE_PF_BK 64
-#endif
-#ifndef MOE_PF_STAGES
-#define MOE_PF_STAGES 2
-#endif
+}  // namespace
 
 // The eight-wave kernel addresses its operands with 32-bit byte offsets: from x for gathered rows,
-// from a tile's first row otherwise, and from an expert's matrix for B.
-bool wave8_fits(const GroupedArgs& a) {
+// from a tile's first row otherwise (256 rows), and from an expert's matrix for B.
+bool bf16_prefill_fits(const GroupedArgs& a) {
   constexpr int64_t LIM = int64_t(1) << 32;
   for (int p = 0; p < 2; ++p) {
     const ExpertProblem& P = a.prob[p];
@@ -791,6 +472,8 @@ bool wave8_fits(const GroupedArgs& a) {
   }
   return true;
 }
+
+namespace {
 
 // Blocks of the persistent kernel: one per CU of the current device (a multiple of 8: every XCD gets
 // the same number), queried once per device.
@@ -816,13 +499,10 @@ hipError_t launch_bm(int bm, const GroupedArgs& a, int64_t max_tile_count, hipSt
   int64_t blocks = (max_tile_count * nc + 7) / 8 * 8;
   if (blocks == 0) return hipSuccess;
   if (bm != 256) return hipErrorInvalidValue;  // the forward builds 256-row tile lists for these kernels
-  if (MOE_PF_EIGHT_WAVES && wave8_fits(a)) {
-    if (!a.work_ctr) return hipErrorInvalidValue;
-    const int64_t grid = min(blocks, persistent_grid());
-    hipLaunchKernelGGL((grouped_bf16_w8<GATE_UP>), dim3((unsigned)grid), dim3(512), 0, s, a, nc);
-  } else
-    hipLaunchKernelGGL((grouped_bf16_lds<256, MOE_PF_BK, MOE_PF_STAGES, GATE_UP>), dim3((unsigned)blocks), dim3(256),
-                       0, s, a, nc);
+  // the host rejects layers beyond the 32-bit offsets before anything is launched
+  if (!bf16_prefill_fits(a) || !a.work_ctr) return hipErrorInvalidValue;
+  const int64_t grid = min(blocks, persistent_grid());
+  hipLaunchKernelGGL((grouped_bf16_w8<GATE_UP>), dim3((unsigned)grid), dim3(512), 0, s, a, nc);
   return hipGetLastError();
 }
 

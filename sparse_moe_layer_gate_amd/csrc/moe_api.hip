@@ -42,10 +42,17 @@ moe_status check_n(const moe_config* c, int64_t N) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// The bf16 prefill GEMM addresses gathered rows of x and each expert matrix with 32-bit byte offsets
+// (gemm_bf16.hip): x of N rows and every [rows, K] weight slab must stay under 4 GiB.
+bool bf16_offsets_fit(int64_t N, int64_t D, int64_t d, int64_t dsh) {
+  constexpr int64_t LIM = int64_t(1) << 32;
+  return N * D * 2 < LIM && d * D * 2 < LIM && dsh * D * 2 < LIM;
+}
+
 size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Workspace {
-  size_t scores, idx, w, chunk_counts, chunk_base, counts, offsets, sorted_pair, inv_row, tiles0, tiles1, ntiles;
+  size_t idx, w, chunk_counts, chunk_base, counts, offsets, sorted_pair, inv_row, tiles0, tiles1, ntiles;
   size_t w3, part, route_total;  // router: split weight, logit partials; bytes moe_route needs
   size_t H, Hsh, Y, Ysh, total;
   RouterPlan rp;
@@ -77,7 +84,6 @@ Workspace layout(const moe_config* c, int64_t N) {
   w.w3 = take(w.rp.split ? sizeof(uint16_t) * 3 * E * D : 0);
   w.part = take(sizeof(float) * w.rp.ks * N * E);
   w.route_total = o;
-  w.scores = take(sizeof(float) * N * E);
   w.idx = take(sizeof(int32_t) * N * k);
   w.w = take(sizeof(float) * N * k);
   w.chunk_counts = take(sizeof(int32_t) * nchunks * E);
@@ -93,6 +99,28 @@ Workspace layout(const moe_config* c, int64_t N) {
   w.Hsh = take(es * N * dsh);
   w.Y = take(es * N * k * D);
   w.Ysh = take(es * N * D);
+  w.total = o;
+  return w;
+}
+
+// Workspace of moe_dispatch on its own: the per-chunk counts and bases (none for a one-chunk batch,
+// which runs as a single kernel).
+struct DispatchWorkspace {
+  size_t chunk_counts, chunk_base, total;
+};
+
+DispatchWorkspace dispatch_layout(const moe_config* c, int64_t N) {
+  DispatchWorkspace w{};
+  const int64_t E = c->n_routed_experts;
+  const int64_t nchunks = N <= kDispatchChunk ? 0 : (N + kDispatchChunk - 1) / kDispatchChunk;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  w.chunk_counts = take(sizeof(int32_t) * nchunks * E);
+  w.chunk_base = take(sizeof(int32_t) * nchunks * E);
   w.total = o;
   return w;
 }
@@ -129,6 +157,7 @@ moe_status check_dense(int64_t N, int32_t D, int32_t dff, int32_t dtype, float l
   if (!std::isfinite(limit) || limit < 0.f) return MOE_ERR_INVALID_ARG;
   if (D % 64 != 0 || dff % 64 != 0 || dff > (1 << 24)) return MOE_ERR_UNSUPPORTED;
   if (N >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
+  if (dtype == MOE_BF16 && !bf16_offsets_fit(256, D, dff, dff)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -138,16 +167,19 @@ T* at(void* ws, size_t off) {
 }
 
 // ---- per-stage timing ----
+// The recording state is per calling thread: moe_profile_begin / _end bracket the calls one thread
+// makes, and calls from other threads are not recorded. The event pool of a thread is reused across
+// recordings and lives until the process ends.
 struct ProfRec {
   int stage;
   hipEvent_t a, b;
 };
-bool g_prof_on = false;
-uint32_t g_prof_mask = 0;  // bit i: record stage i
-bool g_prof_err = false;
-std::vector<ProfRec> g_recs;
-std::vector<hipEvent_t> g_pool;
-size_t g_pool_next = 0;
+thread_local bool g_prof_on = false;
+thread_local uint32_t g_prof_mask = 0;  // bit i: record stage i
+thread_local bool g_prof_err = false;
+thread_local std::vector<ProfRec> g_recs;
+thread_local std::vector<hipEvent_t> g_pool;
+thread_local size_t g_pool_next = 0;
 
 hipEvent_t next_event() {
   if (g_pool_next == g_pool.size()) {
@@ -173,16 +205,22 @@ const char* kStageNames[ST_COUNT_STAGES] = {"router_split", "router_logits", "ro
     if (e_ != hipSuccess) return MOE_ERR_HIP; \
   } while (0)
 
-moe_status route_impl(const moe_config* c, int64_t N, const void* x, const float* wg, const float* bias,
-                      float* scores, uint32_t flags, int32_t* idx, float* w, void* ws, const Workspace& L,
-                      hipStream_t s) {
+// Router. wg is the float32 router weight, or (prepared) the three bf16 pieces of moe_router_prepare;
+// scores is read (MOE_ROUTE_SCORES_IN), written (non-null otherwise) or not kept (null).
+moe_status route_impl(const moe_config* c, int64_t N, const void* x, const void* wg, bool prepared,
+                      const float* bias, float* scores, bool scores_in, int32_t* idx, float* w, void* ws,
+                      const Workspace& L, hipStream_t s) {
   const int E = c->n_routed_experts, D = c->hidden_size;
   float* part = nullptr;
-  if (!(flags & MOE_ROUTE_SCORES_IN)) {
-    uint16_t* w3 = at<uint16_t>(ws, L.w3);
+  if (!scores_in) {
+    const uint16_t* w3 = (const uint16_t*)wg;
     part = at<float>(ws, L.part);
-    if (L.rp.split) MOE_TRY(ST_ROUTER_SPLIT, launch_router_split(wg, E, D, w3, s));
-    MOE_TRY(ST_LOGITS, launch_logits(c->dtype, L.rp, x, wg, w3, N, D, E, part, s));
+    if (L.rp.split && !prepared) {
+      uint16_t* split = at<uint16_t>(ws, L.w3);
+      MOE_TRY(ST_ROUTER_SPLIT, launch_router_split((const float*)wg, E, D, split, s));
+      w3 = split;
+    }
+    MOE_TRY(ST_LOGITS, launch_logits(c->dtype, L.rp, x, (const float*)wg, w3, N, D, E, part, s));
   }
   // alpha on the routed output instead: the weights carry a factor 1, which the product leaves exact
   const float alpha_w = c->alpha_on_output ? 1.0f : c->routed_scaling_factor;
@@ -191,18 +229,34 @@ moe_status route_impl(const moe_config* c, int64_t N, const void* x, const float
   return MOE_OK;
 }
 
+// Dispatch: one kernel for a one-chunk batch, else count / scan / place over per-chunk scratch. t0, t1:
+// the tile lists to build (tiles == nullptr: none, for moe_dispatch on its own).
 moe_status dispatch_impl(const moe_config* c, int64_t N, const int32_t* idx, int32_t* counts, int32_t* offsets,
-                         int32_t* sorted_pair, int32_t* inv_row, void* ws, const Workspace& L, hipStream_t s) {
+                         int32_t* sorted_pair, int32_t* inv_row, int32_t* chunk_counts, int32_t* chunk_base,
+                         const TileSpec& t0, const TileSpec& t1, int pick, hipStream_t s) {
   const int E = c->n_routed_experts, k = c->num_experts_per_tok;
+  const int shared = c->n_shared_experts > 0;
+  if (N <= kDispatchChunk) {
+    MOE_TRY(ST_COUNT, launch_dispatch_small(idx, N, k, E, shared, counts, offsets, sorted_pair, inv_row, t0, t1,
+                                            pick, s));
+    return MOE_OK;
+  }
   const int nchunks = (int)((N + kDispatchChunk - 1) / kDispatchChunk);
-  int32_t* ntiles = at<int32_t>(ws, L.ntiles);
-  TileSpec t0{L.bm0, at<Tile>(ws, L.tiles0), ntiles, small_expert_rows(c->dtype, L.bm0), ntiles + 2};
-  TileSpec t1{L.bm1, at<Tile>(ws, L.tiles1), ntiles + 1, small_expert_rows(c->dtype, L.bm1), ntiles + 10};
-  MOE_TRY(ST_COUNT, launch_count(idx, N, k, E, at<int32_t>(ws, L.chunk_counts), s));
-  MOE_TRY(ST_SCAN, launch_scan(at<int32_t>(ws, L.chunk_counts), nchunks, N, k, E, c->n_shared_experts > 0, counts,
-                               offsets, at<int32_t>(ws, L.chunk_base), t0, t1, L.pick, s));
-  MOE_TRY(ST_PLACE, launch_place(idx, N, k, E, at<int32_t>(ws, L.chunk_base), sorted_pair, inv_row, s));
+  MOE_TRY(ST_COUNT, launch_count(idx, N, k, E, chunk_counts, s));
+  MOE_TRY(ST_SCAN, launch_scan(chunk_counts, nchunks, N, k, E, shared, counts, offsets, chunk_base, t0, t1, pick, s));
+  MOE_TRY(ST_PLACE, launch_place(idx, N, k, E, chunk_base, sorted_pair, inv_row, s));
   return MOE_OK;
+}
+
+// The forward's dispatch: both tile lists in the workspace.
+moe_status forward_dispatch(const moe_config* c, int64_t N, const int32_t* idx, void* ws, const Workspace& L,
+                            hipStream_t s) {
+  int32_t* ntiles = at<int32_t>(ws, L.ntiles);
+  const TileSpec t0{L.bm0, at<Tile>(ws, L.tiles0), ntiles, small_expert_rows(c->dtype, L.bm0), ntiles + 2};
+  const TileSpec t1{L.bm1, at<Tile>(ws, L.tiles1), ntiles + 1, small_expert_rows(c->dtype, L.bm1), ntiles + 10};
+  return dispatch_impl(c, N, idx, at<int32_t>(ws, L.counts), at<int32_t>(ws, L.offsets),
+                       at<int32_t>(ws, L.sorted_pair), at<int32_t>(ws, L.inv_row), at<int32_t>(ws, L.chunk_counts),
+                       at<int32_t>(ws, L.chunk_base), t0, t1, L.pick, s);
 }
 
 // One grouped GEMM over the workspace's tile list `list` (0 or 1), with the 8 work counters at `ctr` in
@@ -260,8 +314,12 @@ moe_status experts_impl(const moe_config* cfg, int64_t N, const void* x, const m
 }
 
 // Host checks shared by the forward entry points: x, y and the expert weights.
-moe_status check_expert_args(const moe_config* cfg, const void* x, const moe_weights* wt, const void* y) {
+moe_status check_expert_args(const moe_config* cfg, int64_t N, const void* x, const moe_weights* wt, const void* y) {
   const bool shared = cfg->n_shared_experts > 0;
+  if (cfg->dtype == MOE_BF16 &&
+      !bf16_offsets_fit(N, cfg->hidden_size, cfg->moe_intermediate_size,
+                        (int64_t)cfg->moe_intermediate_size * cfg->n_shared_experts))
+    return MOE_ERR_UNSUPPORTED;
   if (!x || !y || !wt->gate_up || !wt->down) return MOE_ERR_INVALID_ARG;
   if (shared && (!wt->sh_gate || !wt->sh_up || !wt->sh_down)) return MOE_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(y) || !aligned16(wt->gate_up) || !aligned16(wt->down)) return MOE_ERR_INVALID_ARG;
@@ -316,22 +374,51 @@ size_t moe_workspace_size(const moe_config* cfg, int64_t N) {
   return most;
 }
 
-moe_status moe_route(const moe_config* cfg, int64_t N, const void* x, const float* w_router, const float* e_bias,
+size_t moe_router_prepared_size(const moe_config* cfg) {
+  if (check_cfg(cfg) != MOE_OK || cfg->dtype != MOE_BF16) return 0;
+  return sizeof(uint16_t) * 3 * (size_t)cfg->n_routed_experts * (size_t)cfg->hidden_size;
+}
+
+moe_status moe_router_prepare(const moe_config* cfg, const float* w_router, void* prepared, size_t bytes,
+                              void* stream) {
+  moe_status st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if (cfg->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;  // float32 layers use w_router as given
+  if (!w_router || !prepared || !aligned16(w_router) || !aligned16(prepared)) return MOE_ERR_INVALID_ARG;
+  if (bytes < moe_router_prepared_size(cfg)) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  MOE_TRY(ST_ROUTER_SPLIT,
+          launch_router_split(w_router, cfg->n_routed_experts, cfg->hidden_size, (uint16_t*)prepared, s));
+  return MOE_OK;
+}
+
+moe_status moe_route(const moe_config* cfg, int64_t N, const void* x, const void* w_router, const float* e_bias,
                      float* scores, uint32_t flags, int32_t* topk_idx, float* topk_w, void* workspace, size_t ws_bytes,
                      void* stream) {
   moe_status st = check_cfg(cfg);
   if (st != MOE_OK) return st;
   if ((st = check_n(cfg, N)) != MOE_OK) return st;
-  if (flags & ~MOE_ROUTE_SCORES_IN) return MOE_ERR_INVALID_ARG;
+  if (flags & ~(MOE_ROUTE_SCORES_IN | MOE_ROUTE_SCORES_OUT | MOE_ROUTE_PREPARED)) return MOE_ERR_INVALID_ARG;
+  const bool scores_in = flags & MOE_ROUTE_SCORES_IN, prepared = flags & MOE_ROUTE_PREPARED;
+  if (scores_in && (flags & (MOE_ROUTE_SCORES_OUT | MOE_ROUTE_PREPARED))) return MOE_ERR_INVALID_ARG;
+  if (prepared && cfg->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (N == 0) return MOE_OK;
-  if (!e_bias || !scores || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
+  if (!e_bias || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
+  if ((scores_in || (flags & MOE_ROUTE_SCORES_OUT)) && !scores) return MOE_ERR_INVALID_ARG;
   const Workspace L = layout(cfg, N);
-  if (!(flags & MOE_ROUTE_SCORES_IN)) {
+  if (!scores_in) {
     if (!x || !w_router) return MOE_ERR_INVALID_ARG;
     if (!aligned16(x) || !aligned16(w_router)) return MOE_ERR_INVALID_ARG;
     if (!workspace || ws_bytes < L.route_total || !aligned16(workspace)) return MOE_ERR_WORKSPACE;
   }
-  return route_impl(cfg, N, x, w_router, e_bias, scores, flags, topk_idx, topk_w, workspace, L, (hipStream_t)stream);
+  float* sc = scores_in || (flags & MOE_ROUTE_SCORES_OUT) ? scores : nullptr;
+  return route_impl(cfg, N, x, w_router, prepared, e_bias, sc, scores_in, topk_idx, topk_w, workspace, L,
+                    (hipStream_t)stream);
+}
+
+size_t moe_dispatch_workspace_size(const moe_config* cfg, int64_t N) {
+  if (check_cfg(cfg) != MOE_OK || check_n(cfg, N) != MOE_OK) return 0;
+  return dispatch_layout(cfg, N).total;
 }
 
 moe_status moe_dispatch(const moe_config* cfg, int64_t N, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
@@ -341,16 +428,18 @@ moe_status moe_dispatch(const moe_config* cfg, int64_t N, const int32_t* topk_id
   if ((st = check_n(cfg, N)) != MOE_OK) return st;
   if (!counts || !offsets) return MOE_ERR_INVALID_ARG;
   if (N > 0 && (!topk_idx || !sorted_pair || !inv_row)) return MOE_ERR_INVALID_ARG;
-  const Workspace L = layout(cfg, N);
-  if (!workspace || ws_bytes < L.total || !aligned16(workspace)) return MOE_ERR_WORKSPACE;
+  const DispatchWorkspace L = dispatch_layout(cfg, N);
+  if (L.total > 0 && (!workspace || ws_bytes < L.total || !aligned16(workspace))) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
   if (N == 0) {
-    // empty lists: zero counts and offsets
-    hipStream_t s = (hipStream_t)stream;
-    if (launch_fill_i32(counts, cfg->n_routed_experts, 0, s) != hipSuccess) return MOE_ERR_HIP;
-    if (launch_fill_i32(offsets, cfg->n_routed_experts + 1, 0, s) != hipSuccess) return MOE_ERR_HIP;
+    // empty lists: counts and offsets are all zero (one fill over both)
+    if (launch_fill2_i32(counts, cfg->n_routed_experts, offsets, cfg->n_routed_experts + 1, 0, s) != hipSuccess)
+      return MOE_ERR_HIP;
     return MOE_OK;
   }
-  return dispatch_impl(cfg, N, topk_idx, counts, offsets, sorted_pair, inv_row, workspace, L, (hipStream_t)stream);
+  const TileSpec none{0, nullptr, nullptr, 0, nullptr};
+  return dispatch_impl(cfg, N, topk_idx, counts, offsets, sorted_pair, inv_row, at<int32_t>(workspace, L.chunk_counts),
+                       at<int32_t>(workspace, L.chunk_base), none, none, 0, s);
 }
 
 moe_status moe_forward(const moe_config* cfg, int64_t N, const void* x, const moe_weights* wt, void* y,
@@ -361,8 +450,12 @@ moe_status moe_forward(const moe_config* cfg, int64_t N, const void* x, const mo
   if ((st = check_n(cfg, N)) != MOE_OK) return st;
   if (!wt) return MOE_ERR_INVALID_ARG;
   if (N == 0) return MOE_OK;
-  if ((st = check_expert_args(cfg, x, wt, y)) != MOE_OK) return st;
-  if (!wt->w_router || !wt->e_bias || !aligned16(wt->w_router)) return MOE_ERR_INVALID_ARG;
+  if ((st = check_expert_args(cfg, N, x, wt, y)) != MOE_OK) return st;
+  if (!wt->e_bias) return MOE_ERR_INVALID_ARG;
+  const bool prepared = wt->w_router_prepared != nullptr;
+  if (prepared && cfg->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  const void* wg = prepared ? wt->w_router_prepared : (const void*)wt->w_router;
+  if (!wg || !aligned16(wg)) return MOE_ERR_INVALID_ARG;
   const Workspace L = layout(cfg, N);
   if (!workspace || ws_bytes < L.total || !aligned16(workspace)) return MOE_ERR_WORKSPACE;
 
@@ -373,11 +466,9 @@ moe_status moe_forward(const moe_config* cfg, int64_t N, const void* x, const mo
   float* w = at<float>(ws, L.w);
   int32_t* counts = at<int32_t>(ws, L.counts);
 
-  if ((st = route_impl(cfg, N, x, wt->w_router, wt->e_bias, at<float>(ws, L.scores), 0, idx, w, ws, L, s)) != MOE_OK)
-    return st;
-  if ((st = dispatch_impl(cfg, N, idx, counts, at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.sorted_pair),
-                          at<int32_t>(ws, L.inv_row), ws, L, s)) != MOE_OK)
-    return st;
+  // the scores are not kept
+  if ((st = route_impl(cfg, N, x, wg, prepared, wt->e_bias, nullptr, false, idx, w, ws, L, s)) != MOE_OK) return st;
+  if ((st = forward_dispatch(cfg, N, idx, ws, L, s)) != MOE_OK) return st;
   if ((st = experts_impl(cfg, N, x, wt, w, y, ws, L, s)) != MOE_OK) return st;
 
   if (topk_idx_out && hipMemcpyAsync(topk_idx_out, idx, sizeof(int32_t) * N * k, hipMemcpyDeviceToDevice, s))
@@ -397,7 +488,7 @@ moe_status moe_forward_routed(const moe_config* cfg, int64_t N, const void* x, c
   if ((st = check_n(cfg, N)) != MOE_OK) return st;
   if (!wt) return MOE_ERR_INVALID_ARG;
   if (N == 0) return MOE_OK;
-  if ((st = check_expert_args(cfg, x, wt, y)) != MOE_OK) return st;
+  if ((st = check_expert_args(cfg, N, x, wt, y)) != MOE_OK) return st;
   if (!topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
   const Workspace L = layout(cfg, N);
   if (!workspace || ws_bytes < L.total || !aligned16(workspace)) return MOE_ERR_WORKSPACE;
@@ -405,9 +496,7 @@ moe_status moe_forward_routed(const moe_config* cfg, int64_t N, const void* x, c
   hipStream_t s = (hipStream_t)stream;
   void* ws = workspace;
   int32_t* counts = at<int32_t>(ws, L.counts);
-  if ((st = dispatch_impl(cfg, N, topk_idx, counts, at<int32_t>(ws, L.offsets), at<int32_t>(ws, L.sorted_pair),
-                          at<int32_t>(ws, L.inv_row), ws, L, s)) != MOE_OK)
-    return st;
+  if ((st = forward_dispatch(cfg, N, topk_idx, ws, L, s)) != MOE_OK) return st;
   if ((st = experts_impl(cfg, N, x, wt, topk_w, y, ws, L, s)) != MOE_OK) return st;
   if (counts_out && hipMemcpyAsync(counts_out, counts, sizeof(int32_t) * cfg->n_routed_experts,
                                    hipMemcpyDeviceToDevice, s))

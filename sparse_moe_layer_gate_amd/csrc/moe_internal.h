@@ -13,7 +13,7 @@ enum Stage {
   ST_ROUTER_SPLIT = 0,  // float32 router weight -> three bfloat16 pieces
   ST_LOGITS,            // gate GEMM + sigmoid -> scores
   ST_SELECT,            // bias, group stage, top-k, weights
-  ST_COUNT,             // per-chunk expert histogram
+  ST_COUNT,             // per-chunk expert histogram (batches of one chunk: the whole dispatch)
   ST_SCAN,              // offsets, chunk bases, tile lists
   ST_PLACE,             // stable placement -> sorted_pair / inv_row
   ST_GATE_UP,           // grouped gate_up GEMM + SwiGLU (routed and shared)
@@ -84,16 +84,17 @@ int router_rows_per_block(int dtype);  // token rows of one logits block (the pl
 hipError_t launch_router_split(const float* wg, int E, int D, uint16_t* w3, hipStream_t s);
 hipError_t launch_logits(int dtype, const RouterPlan& p, const void* x, const float* wg, const uint16_t* w3, int64_t N,
                          int D, int E, float* part, hipStream_t s);
-// part == nullptr: scores are an input; otherwise scores are formed from the KS partials and written.
+// part == nullptr: scores are an input; otherwise scores are formed from the KS partials and written
+// (unless scores == nullptr).
 hipError_t launch_select(float* scores, const float* part, int KS, const float* bias, int64_t N, int E, int G, int TG,
                          int k, float alpha, int norm, float eps, int32_t* idx, float* w, hipStream_t s);
 
 // ---- dispatch ----
 struct TileSpec {
   int bm;            // rows per tile
-  Tile* tiles;       // output list
+  Tile* tiles;       // output list (nullptr: no list is built)
   int32_t* n_tiles;  // output count
-  int small_max;     // > 0: tiles of experts with 1..small_max rows are spread evenly among the others
+  int small_max;     // > 0: tiles of experts with 1..small_max rows go after all the others
   int32_t* work_ctr;  // the list's 8 work counters (persistent kernels), zeroed with the list; or nullptr
 };
 hipError_t launch_count(const int32_t* idx, int64_t N, int k, int E, int32_t* chunk_counts, hipStream_t s);
@@ -104,6 +105,10 @@ hipError_t launch_scan(const int32_t* chunk_counts, int nchunks, int64_t N, int 
 hipError_t launch_dense_tiles(int64_t N, TileSpec t0, TileSpec t1, hipStream_t s);
 hipError_t launch_place(const int32_t* idx, int64_t N, int k, int E, const int32_t* chunk_base, int32_t* sorted_pair,
                         int32_t* inv_row, hipStream_t s);
+// count + scan + place in one block for N <= kDispatchChunk (same results as the three kernels)
+hipError_t launch_dispatch_small(const int32_t* idx, int64_t N, int k, int E, int n_shared_problem, int32_t* counts,
+                                 int32_t* offsets, int32_t* sorted_pair, int32_t* inv_row, TileSpec t0, TileSpec t1,
+                                 int pick_rows, hipStream_t s);
 
 // ---- grouped expert GEMMs ----
 struct ExpertProblem {
@@ -182,5 +187,7 @@ hipError_t launch_combine(int dtype, const void* Y, const void* Ysh, const int32
                           float alpha_out, void* y, hipStream_t s);
 // p[0 .. n) = v (a kernel rather than a memset node, so the call may sit in a captured graph)
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
+// p[0 .. n) = v and q[0 .. m) = v in one launch
+hipError_t launch_fill2_i32(int32_t* p, int64_t n, int32_t* q, int64_t m, int32_t v, hipStream_t s);
 
 }  // namespace moe

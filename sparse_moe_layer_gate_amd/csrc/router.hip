@@ -263,7 +263,7 @@ __global__ __launch_bounds__(256) void logits_f32_kernel(const XT* __restrict__ 
 // ---------------------------------------------------------------------------------------------
 // Selection: one wavefront per token, four tokens per block. Lane l holds experts l, l + 64, ...
 // (up to 8). With `part` set, the scores are first formed from the KS logit partials (added in
-// order) and written out; otherwise they are read. Every float operation of the selection is one
+// order) and written out when `scores` is set; otherwise they are read from `scores`. Every float operation of the selection is one
 // correctly rounded IEEE operation in the order the header states, so given the same scores the
 // result is bit-identical to a plain float32 evaluation.
 constexpr int SEL_MAX_E = 512, SEL_MAX_P = SEL_MAX_E / 64, SEL_MAX_G = 64, SEL_MAX_K = 32;
@@ -331,7 +331,7 @@ __global__ __launch_bounds__(256) void select_kernel(float* __restrict__ scores,
     float sv = 0.f, bv = 0.f;
     if (p < P && e < E && live) {
       sv = sraw[p];
-      if (part) scores[n * E + e] = sv;
+      if (part && scores) scores[n * E + e] = sv;  // the forward does not keep them
       bv = bias[e];
     }
     sp[p] = __fadd_rn(sv, bv);  // s' = s + b

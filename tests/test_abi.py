@@ -130,7 +130,8 @@ def test_argument_errors_before_any_launch():
     st = L.moe_forward(ctypes.byref(cfg), 4, ctypes.c_void_p(8192), ctypes.byref(ws), ctypes.c_void_p(12288), None,
                        None, None, fake, 16, None)
     assert st == moe.MOE_ERR_WORKSPACE
-    st = L.moe_dispatch(ctypes.byref(cfg), 4, fake, fake, fake, fake, fake, fake, 16, None)
+    # batches of more than one 256-token chunk need the per-chunk scratch
+    st = L.moe_dispatch(ctypes.byref(cfg), 1000, fake, fake, fake, fake, fake, fake, 16, None)
     assert st == moe.MOE_ERR_WORKSPACE
     # N = 0 with nothing else given is a valid no-op for the router and the forward
     assert L.moe_route(ctypes.byref(cfg), 0, None, None, None, None, 0, None, None, None, 0, None) == moe.MOE_OK
@@ -167,3 +168,63 @@ def test_dense_sizes_and_errors():
                                None) == moe.MOE_ERR_WORKSPACE
     assert L.moe_dense_forward(0, 256, 128, moe.MOE_BF16, ctypes.c_float(0.0), None, None, None, None, None, None, 0,
                                None) == moe.MOE_OK
+
+
+def test_route_flags():
+    """SCORES_IN excludes SCORES_OUT and PREPARED; PREPARED needs a bf16 layer; SCORES_OUT needs scores."""
+    L = moe.lib()
+    fake = ctypes.c_void_p(4096)  # never dereferenced
+    f32 = moe.config_of(synth.WORKLOADS["tiny_fp32"])
+    bf = moe.config_of(synth.WORKLOADS["glm5_decode"])
+    for cfg, flags in [(bf, moe.MOE_ROUTE_SCORES_IN | moe.MOE_ROUTE_SCORES_OUT),
+                       (bf, moe.MOE_ROUTE_SCORES_IN | moe.MOE_ROUTE_PREPARED), (f32, moe.MOE_ROUTE_PREPARED)]:
+        assert L.moe_route(ctypes.byref(cfg), 4, fake, fake, fake, fake, flags, fake, fake, fake, 1 << 30,
+                           None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_route(ctypes.byref(bf), 4, fake, fake, fake, None, moe.MOE_ROUTE_SCORES_OUT, fake, fake, fake,
+                       1 << 30, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_route(ctypes.byref(bf), 4, fake, fake, fake, None, 0, fake, fake, fake, 16,
+                       None) == moe.MOE_ERR_WORKSPACE  # scores may be null; the short workspace is the error
+
+
+def test_router_prepare_sizes_and_errors():
+    L = moe.lib()
+    fake = ctypes.c_void_p(4096)
+    w = synth.WORKLOADS["glm5_decode"]
+    bf = moe.config_of(w)
+    assert moe.moe_router_prepared_size(bf) == 3 * w.E * w.D * 2
+    assert moe.moe_router_prepared_size(moe.config_of(synth.WORKLOADS["tiny_fp32"])) == 0
+    f32 = moe.config_of(synth.WORKLOADS["tiny_fp32"])
+    assert L.moe_router_prepare(ctypes.byref(f32), fake, fake, 1 << 30, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_router_prepare(ctypes.byref(bf), None, fake, 1 << 30, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_router_prepare(ctypes.byref(bf), fake, fake, 16, None) == moe.MOE_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("name", ["glm5_prefill", "tiny_fp32", "glm45_prefill_skewed"])
+def test_dispatch_workspace_size(name):
+    """moe_dispatch's own scratch: none for one chunk of 256 tokens, per-chunk counts above, never
+    falling, and far below the forward's workspace."""
+    cfg = moe.config_of(synth.WORKLOADS[name])
+    sizes = np.array([moe.moe_dispatch_workspace_size(cfg, n) for n in range(0, 3000, 7)], dtype=np.int64)
+    assert (np.diff(sizes) >= 0).all()
+    assert moe.moe_dispatch_workspace_size(cfg, 256) == 0 and moe.moe_dispatch_workspace_size(cfg, 257) > 0
+    assert moe.moe_dispatch_workspace_size(cfg, 8192) * 100 < moe.moe_workspace_size(cfg, 8192)
+    assert moe.moe_dispatch_workspace_size(cfg, -1) == 0
+
+
+def test_bf16_offsets_limit():
+    """The bf16 prefill GEMM addresses x and each expert matrix with 32-bit byte offsets: a batch whose x
+    reaches 4 GiB, or a dense FFN whose weight matrices do, is MOE_ERR_UNSUPPORTED before any launch."""
+    L = moe.lib()
+    fake = ctypes.c_void_p(4096)
+    w = synth.WORKLOADS["glm5_prefill"]
+    cfg = moe.config_of(w)
+    N = (1 << 32) // (2 * w.D) + 1
+    ws = moe.MoeWeights(fake, fake, fake, fake, fake, fake, fake)
+    x, y = ctypes.c_void_p(8192), ctypes.c_void_p(12288)
+    assert L.moe_forward(ctypes.byref(cfg), N, x, ctypes.byref(ws), y, None, None, None, fake, 1 << 40,
+                         None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_forward_routed(ctypes.byref(cfg), N, x, ctypes.byref(ws), fake, fake, y, None, fake, 1 << 40,
+                                None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_dense_forward(4, 65536, 32768, moe.MOE_BF16, ctypes.c_float(0.0), x, fake, fake, fake, y, fake,
+                               1 << 40, None) == moe.MOE_ERR_UNSUPPORTED
+    assert moe.moe_dense_workspace_size(4, 65536, 32768, "bf16") == 0

@@ -60,7 +60,8 @@ def route_gpu(w, x_dev, dev):
     s = torch.empty((N, w.E), dtype=torch.float32, device="cuda")
     idx = torch.empty((N, w.k), dtype=torch.int32, device="cuda")
     wt = torch.empty((N, w.k), dtype=torch.float32, device="cuda")
-    moe.moe_route(cfg, N, x_dev, dev["w_router"], dev["e_bias"], s, idx, wt, workspace=moe.alloc_workspace(cfg, N))
+    moe.moe_route(cfg, N, x_dev, dev["w_router"], dev["e_bias"], s, idx, wt, flags=moe.MOE_ROUTE_SCORES_OUT,
+                  workspace=moe.alloc_workspace(cfg, N))
     torch.cuda.synchronize()
     return H.to_host(s), H.to_host(idx), H.to_host(wt)
 
@@ -118,6 +119,23 @@ def test_forward_deterministic_and_permutation_equivariant():
     perm = np.random.default_rng(0).permutation(w.N)
     y3, i3, w3, _ = H.gpu_forward(w, H.to_device(x[perm]), dev)
     assert np.array_equal(y3, y1[perm]) and np.array_equal(i3, i1[perm]) and np.array_equal(w3, w1[perm])
+
+
+@pytest.mark.parametrize("name", ["glm5_decode", "air_prefill"])
+def test_forward_prepared_router_bitexact(name):
+    """The forward on moe_router_prepare's output (the split taken once) equals the forward that splits
+    the float32 router weight itself, bit for bit."""
+    import sparse_moe_layer_gate_amd as moe
+
+    w = synth.WORKLOADS[name]
+    _, _, dev = H.device_weights(w, generate_on_device=True)
+    x_dev = H.to_device(synth.x_host(w))
+    y1, i1, w1, c1 = H.gpu_forward(w, x_dev, dev)
+    dev2 = dict(dev)
+    dev2["w_router_prepared"] = moe.moe_router_prepare(moe.config_of(w), dev["w_router"])
+    del dev2["w_router"]
+    y2, i2, w2, c2 = H.gpu_forward(w, x_dev, dev2)
+    assert np.array_equal(y1, y2) and np.array_equal(i1, i2) and np.array_equal(w1, w2) and np.array_equal(c1, c2)
 
 
 def test_device_generator_matches_host():

@@ -35,7 +35,7 @@ def _route_gpu(w, N, s_host=None, x_host=None, wg=None, b=None):
     else:
         s_d = torch.empty((N, w.E), dtype=torch.float32, device="cuda")
         moe.moe_route(cfg, N, H.to_device(x_host), H.to_device(wg), b_d, s_d, idx, wt,
-                      workspace=moe.alloc_workspace(cfg, N))
+                      flags=moe.MOE_ROUTE_SCORES_OUT, workspace=moe.alloc_workspace(cfg, N))
     torch.cuda.synchronize()
     return H.to_host(s_d), H.to_host(idx), H.to_host(wt)
 
@@ -182,6 +182,61 @@ def test_dispatch_random(N, E, k, skew):
     ref = oracle.dispatch(w, idx)
     for g, r, what in zip(got, ref, ["counts", "offsets", "sorted_pair", "inv_row"]):
         assert np.array_equal(g, r), what
+
+
+@pytest.mark.parametrize("N", [1, 200, 256, 257, 5000])
+def test_dispatch_own_workspace(N):
+    """moe_dispatch with a workspace of exactly moe_dispatch_workspace_size bytes (none for a batch of one
+    256-token chunk, which runs as one kernel; per-chunk scratch above) is bit-exact."""
+    import torch
+
+    import sparse_moe_layer_gate_amd as moe
+
+    w = replace(synth.WORKLOADS["tiny_fp32"], N=N, E=64, G=8, TG=4, k=6)
+    rng = np.random.default_rng(N)
+    idx = np.argsort(rng.random((N, w.E)), axis=1)[:, :w.k].astype(np.int32)
+    cfg = moe.config_of(w)
+    size = moe.moe_dispatch_workspace_size(cfg, N)
+    assert (size == 0) == (N <= 256)
+    ws = torch.empty(size, dtype=torch.uint8, device="cuda") if size else None
+    counts = torch.empty(w.E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(w.E + 1, dtype=torch.int32, device="cuda")
+    sp = torch.empty(N * w.k, dtype=torch.int32, device="cuda")
+    inv = torch.empty(N * w.k, dtype=torch.int32, device="cuda")
+    moe.moe_dispatch(cfg, N, H.to_device(idx), counts, offsets, sp, inv, ws)
+    torch.cuda.synchronize()
+    for g, r, what in zip((counts, offsets, sp, inv), oracle.dispatch(w, idx), ["counts", "offsets", "sp", "inv"]):
+        assert np.array_equal(H.to_host(g), r), what
+
+
+@pytest.mark.parametrize("name", ["glm5_decode", "air_prefill"])
+def test_route_prepared_and_without_scores(name):
+    """moe_route on the prepared router weight (moe_router_prepare) gives the same scores, ids and weights,
+    bit for bit, as on the float32 weight; without MOE_ROUTE_SCORES_OUT the ids and weights are the same
+    and no scores are needed."""
+    import torch
+
+    import sparse_moe_layer_gate_amd as moe
+
+    w = synth.WORKLOADS[name]
+    x = synth.x_host(w)
+    wg, b = synth.router_host(w)
+    cfg = moe.config_of(w)
+    x_d, wg_d, b_d = H.to_device(x), H.to_device(wg), H.to_device(b)
+    prep = moe.moe_router_prepare(cfg, wg_d)
+    ws = moe.alloc_workspace(cfg, w.N)
+    outs = []
+    for weight, flags in [(wg_d, moe.MOE_ROUTE_SCORES_OUT), (prep, moe.MOE_ROUTE_SCORES_OUT | moe.MOE_ROUTE_PREPARED),
+                          (wg_d, 0), (prep, moe.MOE_ROUTE_PREPARED)]:
+        s = torch.full((w.N, w.E), -1.0, device="cuda") if flags & moe.MOE_ROUTE_SCORES_OUT else None
+        idx = torch.empty((w.N, w.k), dtype=torch.int32, device="cuda")
+        wt = torch.empty((w.N, w.k), dtype=torch.float32, device="cuda")
+        moe.moe_route(cfg, w.N, x_d, weight, b_d, s, idx, wt, flags=flags, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append((None if s is None else H.to_host(s), H.to_host(idx), H.to_host(wt)))
+    assert np.array_equal(outs[0][0].view(np.uint32), outs[1][0].view(np.uint32))
+    for o in outs[1:]:
+        assert np.array_equal(o[1], outs[0][1]) and np.array_equal(o[2].view(np.uint32), outs[0][2].view(np.uint32))
 
 
 def test_dispatch_leaves_out_invalid_ids():
