@@ -39,7 +39,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 #define MOE_DC_WEIGHT_CPOL 2
 #endif
 
-template <bool GATE_UP>
+template <bool GATE_UP, int WPB>
 struct DecodeTile {
   static constexpr int NT = MOE_DC_NT;  // 16-column weight tiles per wave
   static constexpr int U = MOE_DC_U;    // 32-wide K slices per stage
@@ -53,7 +53,7 @@ struct DecodeTile {
   static constexpr int WAVE_BYTES = S * STAGE_BYTES;
   static constexpr int NDMA = (NT + 1) * QPT;  // DMA instructions per stage
   static constexpr int WAVE_COLS = GATE_UP ? NT / 2 * 16 : NT * 16;  // output columns per wave
-  static constexpr int BLOCK_COLS = 4 * WAVE_COLS;
+  static constexpr int BLOCK_COLS = WPB * WAVE_COLS;  // WPB waves per block
   static_assert(!GATE_UP || NT % 2 == 0, "gate_up pairs gate and up tiles");
   static_assert(CPR >= 8 && CPR <= 64 && 64 % CPR == 0, "a DMA instruction covers whole 128-byte lines");
   static_assert((S - 1) * NDMA < 64, "vmcnt is 6 bits");
@@ -64,11 +64,11 @@ struct DecodeTile {
   __device__ static int sig(int r) { return CPR >= 16 ? r : r / (16 / CPR); }
 };
 
-template <bool GATE_UP>
-__global__ __launch_bounds__(256) void grouped_bf16_decode(GroupedArgs a, int ncol_max) {
-  using T = DecodeTile<GATE_UP>;
+template <bool GATE_UP, int WPB>
+__global__ __launch_bounds__(64 * WPB) void grouped_bf16_decode(GroupedArgs a, int ncol_max) {
+  using T = DecodeTile<GATE_UP, WPB>;
   constexpr int NT = T::NT, U = T::U, S = T::S, SK = T::SK, CPR = T::CPR, RPI = T::RPI, QPT = T::QPT;
-  __shared__ __attribute__((aligned(1024))) char lds[4 * T::WAVE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds[WPB * T::WAVE_BYTES];
 
   const int64_t L = xcd_logical_block((int64_t)*a.n_tiles * ncol_max);
   if (L < 0) return;
@@ -189,15 +189,33 @@ __global__ __launch_bounds__(256) void grouped_bf16_decode(GroupedArgs a, int nc
   }
 }
 
+#ifndef MOE_DC_ONE_WAVE_BLOCKS
+#define MOE_DC_ONE_WAVE_BLOCKS 1024
+#endif
+
+template <bool GATE_UP, int WPB>
+int64_t decode_blocks(const GroupedArgs& a, int64_t max_tile_count, int* nc) {
+  constexpr int BLOCK_COLS = DecodeTile<GATE_UP, WPB>::BLOCK_COLS;
+  *nc = 0;
+  for (int p = 0; p < 2; ++p)
+    if (a.prob[p].out) *nc = max(*nc, (a.prob[p].ncols + BLOCK_COLS - 1) / BLOCK_COLS);
+  return (max_tile_count * *nc + 7) / 8 * 8;
+}
+
+// Four-wave blocks, or one-wave blocks when a batch has too few tiles to give every CU several blocks
+// (a few tokens: at one token the 9 tiles of GLM-5 make 288 four-wave blocks for 256 CUs, so a quarter
+// of the CUs stream twice as long as the rest); the waves work alone either way.
 template <bool GATE_UP>
 hipError_t launch(const GroupedArgs& a, int64_t max_tile_count, hipStream_t s) {
-  constexpr int BLOCK_COLS = DecodeTile<GATE_UP>::BLOCK_COLS;
   int nc = 0;
-  for (int p = 0; p < 2; ++p)
-    if (a.prob[p].out) nc = max(nc, (a.prob[p].ncols + BLOCK_COLS - 1) / BLOCK_COLS);
-  const int64_t blocks = (max_tile_count * nc + 7) / 8 * 8;
+  int64_t blocks = decode_blocks<GATE_UP, 4>(a, max_tile_count, &nc);
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(grouped_bf16_decode<GATE_UP>, dim3((unsigned)blocks), dim3(256), 0, s, a, nc);
+  if (blocks < MOE_DC_ONE_WAVE_BLOCKS) {
+    blocks = decode_blocks<GATE_UP, 1>(a, max_tile_count, &nc);
+    hipLaunchKernelGGL((grouped_bf16_decode<GATE_UP, 1>), dim3((unsigned)blocks), dim3(64), 0, s, a, nc);
+  } else {
+    hipLaunchKernelGGL((grouped_bf16_decode<GATE_UP, 4>), dim3((unsigned)blocks), dim3(256), 0, s, a, nc);
+  }
   return hipGetLastError();
 }
 
