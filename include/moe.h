@@ -178,6 +178,20 @@ moe_status moe_forward(const moe_config* cfg, int64_t N, const void* x, const mo
                        int32_t* topk_idx_out, float* topk_w_out, int32_t* counts_out, void* workspace,
                        size_t ws_bytes, void* stream);
 
+/* moe_forward without a workspace argument, for callers that cannot allocate device memory: code being
+ * captured into a HIP graph, serving loops that must not call the allocator, harnesses that forbid it.
+ * The scratch is a fixed device array of moe_noalloc_scratch_bytes() (32 MiB) inside the library, one
+ * per device, taken from the first call on each device until the process ends. The call allocates and
+ * frees nothing; it returns MOE_ERR_WORKSPACE, before launching anything, when the batch needs more than
+ * that (moe_workspace_size(cfg, N) > moe_noalloc_scratch_bytes(): on the GLM-5 shape batches of up to
+ * 146 tokens fit), and MOE_ERR_HIP if the array's device address cannot be found. Every call on a
+ * device shares that device's array: calls that may overlap on one device (other streams, other
+ * threads) race and must be serialised by the caller. No part of the array has to start at zero: each
+ * call writes every region it reads. Arguments and results otherwise as moe_forward. */
+moe_status moe_forward_noalloc(const moe_config* cfg, int64_t N, const void* x, const moe_weights* w, void* y,
+                               int32_t* topk_idx_out, float* topk_w_out, int32_t* counts_out, void* stream);
+size_t moe_noalloc_scratch_bytes(void);
+
 /* The layer with routing given by the caller ("MoE Forward", Official code: the experts take x, the
  * top-k indices and the top-k weights; "GLM-5 . Mixture of experts": the expert loop skips id E):
  * dispatch, routed experts, combine and shared expert as in moe_forward, without the router.

@@ -20,7 +20,8 @@ MOE_ROUTE_SCORES_IN, MOE_ROUTE_SCORES_OUT, MOE_ROUTE_PREPARED = 1, 2, 4
 
 EXPORTED = ["moe_check_config", "moe_workspace_size", "moe_dispatch_workspace_size", "moe_router_prepared_size",
             "moe_router_prepare", "moe_route", "moe_dispatch", "moe_forward", "moe_forward_routed",
-            "moe_dense_workspace_size", "moe_dense_forward", "moe_status_str", "moe_profile_begin",
+            "moe_forward_noalloc", "moe_noalloc_scratch_bytes", "moe_dense_workspace_size", "moe_dense_forward",
+            "moe_status_str", "moe_profile_begin",
             "moe_profile_begin_mask", "moe_profile_end", "moe_stage_name", "moe_stage_count"]
 
 
@@ -82,6 +83,10 @@ def lib():
         L.moe_forward.argtypes = [cp, i64, vp, ctypes.POINTER(MoeWeights), vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.moe_forward_routed.argtypes = [cp, i64, vp, ctypes.POINTER(MoeWeights), vp, vp, vp, vp, vp,
                                          ctypes.c_size_t, vp]
+        L.moe_forward_noalloc.argtypes = [cp, i64, vp, ctypes.POINTER(MoeWeights), vp, vp, vp, vp, vp]
+        L.moe_forward_noalloc.restype = ctypes.c_int
+        L.moe_noalloc_scratch_bytes.argtypes = []
+        L.moe_noalloc_scratch_bytes.restype = ctypes.c_size_t
         L.moe_dense_workspace_size.argtypes = [i64, i32, i32, i32]
         L.moe_dense_workspace_size.restype = ctypes.c_size_t
         L.moe_dense_forward.argtypes = [i64, i32, i32, i32, ctypes.c_float, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,

@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <vector>
 
 #include "moe_internal.h"
@@ -329,6 +330,30 @@ moe_status check_expert_args(const moe_config* cfg, int64_t N, const void* x, co
   return MOE_OK;
 }
 
+// ---- scratch for moe_forward_noalloc ----
+// A fixed device array that stands in for the caller's workspace. In host code `scratch` names a host
+// stand-in, not device memory: its device address is taken once per device with hipGetSymbolAddress
+// (scratch_on_current_device) and only that address is used.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch`, or nullptr if the device or the symbol lookup fails.
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 namespace moe {
@@ -502,6 +527,21 @@ moe_status moe_forward_routed(const moe_config* cfg, int64_t N, const void* x, c
                                    hipMemcpyDeviceToDevice, s))
     return MOE_ERR_HIP;
   return MOE_OK;
+}
+
+size_t moe_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+moe_status moe_forward_noalloc(const moe_config* cfg, int64_t N, const void* x, const moe_weights* w, void* y,
+                               int32_t* topk_idx_out, float* topk_w_out, int32_t* counts_out, void* stream) {
+  moe_status st = check_cfg(cfg);
+  if (st != MOE_OK) return st;
+  if ((st = check_n(cfg, N)) != MOE_OK) return st;
+  if (N == 0) return w ? MOE_OK : MOE_ERR_INVALID_ARG;
+  const size_t need = layout(cfg, N).total;
+  if (need > kScratchBytes) return MOE_ERR_WORKSPACE;  // the batch needs more than the fixed scratch
+  void* ws = scratch_on_current_device();
+  if (!ws) return MOE_ERR_HIP;
+  return moe_forward(cfg, N, x, w, y, topk_idx_out, topk_w_out, counts_out, ws, kScratchBytes, stream);
 }
 
 size_t moe_dense_workspace_size(int64_t N, int32_t D, int32_t dff, int32_t dtype) {
