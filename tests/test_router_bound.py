@@ -16,7 +16,7 @@ import oracle
 import synth
 from tests import _harness as H
 
-BF16_WORKLOADS = ["air_prefill", "glm45_prefill_skewed", "glm5_prefill"]
+BF16_WORKLOADS = ["air_prefill", "glm45_prefill_skewed", "glm5_prefill", "glm45_prefill_mild_skew"]
 
 
 def _inputs(name, tokens):
