@@ -76,6 +76,7 @@ constexpr int kDispatchChunk = 256;  // tokens per dispatch block
 // ---- router ----
 struct RouterPlan {
   bool split;  // bf16 activations: the router weight runs as three bf16 pieces on the bf16 matrix cores
+  bool gemv;   // split, and few enough tokens for the one-wave-per-expert kernel (ks = 1)
   int ks;      // partial sums per logit (split of the hidden dimension)
   int kchunk;  // hidden elements per split (a multiple of 32)
 };

@@ -190,6 +190,83 @@ int router_nj(int64_t N, int E) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// Cross-lane steps on the DPP paths (no LDS round trip). dpp<CTRL>(v): lane i reads v of the lane CTRL
+// names; the four patterns used are permutations of each 16-lane row, so every lane has a source.
+constexpr int DPP_QUAD_XOR1 = 0xB1;     // quad_perm [1, 0, 3, 2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;     // quad_perm [2, 3, 0, 1]
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;  // lane i <- lane 7 - i within each 8 lanes
+constexpr int DPP_ROW_MIRROR = 0x140;       // lane i <- lane 15 - i within each 16 lanes
+template <int CTRL>
+__device__ inline int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ inline float dpp_f(float v) {
+  return __int_as_float(dpp_i<CTRL>(__float_as_int(v)));
+}
+__device__ inline float readlane_f(float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); }
+
+// Sum of v over the 64 lanes, the same value in every lane. Each step adds a lane's value to its
+// partner's within a 16-lane row (a + b == b + a, so both partners hold the same sum), then the four
+// row sums are added as (r0 + r1) + (r2 + r3).
+__device__ inline float wave_sum(float v) {
+  v += dpp_f<DPP_QUAD_XOR1>(v);
+  v += dpp_f<DPP_QUAD_XOR2>(v);
+  v += dpp_f<DPP_ROW_HALF_MIRROR>(v);
+  v += dpp_f<DPP_ROW_MIRROR>(v);
+  return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
+}
+
+// ---------------------------------------------------------------------------------------------
+// bf16 gate GEMV for batches of at most RG_MAX_N tokens: part[0, n, e] = x[n] (lo + mid + hi)[e]^T
+// over the whole hidden dimension (one partial per logit). A one-wave block per expert: lane l takes
+// the 16-byte chunks l, l + 64, ... of the expert's three pieces and of every token's row, adds
+// x * lo, x * mid, x * hi per element in float32 (each product exact), and the wave sums its lanes. The
+// matrix-core kernel spends a 128-token block on a batch of one token and has too few blocks to spread
+// the router weight's stream over the CUs.
+constexpr int RG_MAX_N = 4;
+template <int NT>
+__global__ __launch_bounds__(64) void logits_gemv_kernel(const uint16_t* __restrict__ x,
+                                                         const uint16_t* __restrict__ w3, int D, int E,
+                                                         float* __restrict__ part) {
+  const int e = blockIdx.x, lane = threadIdx.x;
+  if (e >= E) return;
+  const int64_t ED = (int64_t)E * D;
+  const uint16_t* wr = w3 + (int64_t)e * D;
+  float acc[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) acc[n] = 0.f;
+  const int nch = D / 8;  // D is a multiple of 64
+#pragma unroll 4
+  for (int c = lane; c < nch; c += 64) {
+    uint4 wv[3], xv[NT];
+#pragma unroll
+    for (int piece = 0; piece < 3; ++piece) wv[piece] = *(const uint4*)(wr + piece * ED + 8 * c);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) xv[n] = *(const uint4*)(x + (int64_t)n * D + 8 * c);
+#pragma unroll
+    for (int h = 0; h < 8; ++h) {
+      const int word = h >> 1, sh = (h & 1) * 16;
+      const float lo = __uint_as_float(((((const uint32_t*)&wv[2])[word] >> sh) & 0xffffu) << 16);
+      const float mid = __uint_as_float(((((const uint32_t*)&wv[1])[word] >> sh) & 0xffffu) << 16);
+      const float hi = __uint_as_float(((((const uint32_t*)&wv[0])[word] >> sh) & 0xffffu) << 16);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const float xf = __uint_as_float(((((const uint32_t*)&xv[n])[word] >> sh) & 0xffffu) << 16);
+        acc[n] = __fmaf_rn(xf, lo, acc[n]);  // exact product: the fma rounds once, as the add would
+        acc[n] = __fmaf_rn(xf, mid, acc[n]);
+        acc[n] = __fmaf_rn(xf, hi, acc[n]);
+      }
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    const float sum = wave_sum(acc[n]);
+    if (lane == 0) part[(int64_t)n * E + e] = sum;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // float32 gate GEMM on v_mfma_f32_16x16x4_f32: part[ks, n, e] over the ks-th hidden range.
 // Block tile: 64 tokens x 64 experts, K step 32; 4 waves in 2 x 2, each 32 x 32 (2 x 2 MFMA tiles).
 // LDS holds both tiles k-major with a row pitch of 80 floats: a wave's MFMA operand read touches
@@ -270,17 +347,25 @@ constexpr int SEL_MAX_E = 512, SEL_MAX_P = SEL_MAX_E / 64, SEL_MAX_G = 64, SEL_M
 constexpr int SEL_MAX_KS = 16;  // logit partials per score (router_plan keeps KS within this)
 
 __device__ inline bool beats(float av, int ai, float bv, int bi) { return av > bv || (av == bv && ai < bi); }
+// (bv, bi) <- the better of this lane's pair and the pair of the lane CTRL names
+template <int CTRL>
+__device__ inline void argmax_row_step(float& bv, int& bi) {
+  const float ov = dpp_f<CTRL>(bv);
+  const int oi = dpp_i<CTRL>(bi);
+  if (beats(ov, oi, bv, bi)) {
+    bv = ov;
+    bi = oi;
+  }
+}
 
 template <int MAXKS>
 __global__ __launch_bounds__(256) void select_kernel(float* __restrict__ scores, const float* __restrict__ part,
                                                      int KS, const float* __restrict__ bias, int64_t N, int E, int G,
                                                      int TG, int k, float alpha, int norm, float eps,
                                                      int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
-  __shared__ float s_raw[4][SEL_MAX_E];
   __shared__ float s_sel[4][SEL_MAX_E];
   __shared__ float gscore[4][SEL_MAX_G];
   __shared__ int kept[4][SEL_MAX_G];
-  __shared__ int chosen[4][SEL_MAX_K];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t n = (int64_t)blockIdx.x * 4 + wave;
@@ -291,7 +376,7 @@ __global__ __launch_bounds__(256) void select_kernel(float* __restrict__ scores,
 
   float sp[SEL_MAX_P];
   bool elig[SEL_MAX_P];
-  float sraw[SEL_MAX_P];
+  float sraw[SEL_MAX_P] = {};
   // Scores: with partials, the KS partials of SEL_PB experts per lane are all loaded before the first
   // add (one memory round trip per group of SEL_PB experts), then added in order q = 0, 1, ... The loads
   // are unconditional, from clamped in-bounds addresses (MAXKS >= KS slots; extra slots repeat partial
@@ -336,25 +421,21 @@ __global__ __launch_bounds__(256) void select_kernel(float* __restrict__ scores,
     }
     sp[p] = __fadd_rn(sv, bv);  // s' = s + b
     elig[p] = p < P && e < E;
-    if (p < P && e < E) {
-      s_raw[wave][e] = sv;
-      s_sel[wave][e] = sp[p];
-    }
+    if (p < P && e < E) s_sel[wave][e] = sp[p];
   }
   __syncthreads();
 
   if (group_stage) {
     // group score: sum of the two largest s' of the group (a repeated value counts twice)
     if (lane < G) {
+      // running top two (m1 >= m2): v above m1 pushes m1 down, v in (m2, m1] replaces m2
       float m1 = -INFINITY, m2 = -INFINITY;
-      for (int e = lane * gs; e < (lane + 1) * gs; ++e) {
-        const float v = s_sel[wave][e];
-        if (v > m1) {
-          m2 = m1;
-          m1 = v;
-        } else if (v > m2) {
-          m2 = v;
-        }
+      const float* gv = &s_sel[wave][lane * gs];
+#pragma unroll 8
+      for (int j = 0; j < gs; ++j) {
+        const float v = gv[j];
+        m2 = fmaxf(m2, fminf(m1, v));
+        m1 = fmaxf(m1, v);
       }
       gscore[wave][lane] = __fadd_rn(m1, m2);
     }
@@ -373,7 +454,12 @@ __global__ __launch_bounds__(256) void select_kernel(float* __restrict__ scores,
     }
   }
 
-  // k rounds of a wave-wide arg-max under (s' descending, index ascending)
+  // k rounds of a wave-wide arg-max under (s' descending, index ascending). beats() is a strict total
+  // order on (value, index) pairs with distinct indices, so the winner does not depend on the order in
+  // which the lanes' candidates meet. The winner's raw score is read from the lane that holds it and
+  // added to the running sum in slot order; lane j keeps slot j.
+  float sum = 0.f, my_s = 0.f;
+  int my_e = 0;
   for (int slot = 0; slot < k; ++slot) {
     float bv = -INFINITY;
     int bi = 0x7fffffff;
@@ -385,35 +471,47 @@ __global__ __launch_bounds__(256) void select_kernel(float* __restrict__ scores,
         bi = e;
       }
     }
+    argmax_row_step<DPP_QUAD_XOR1>(bv, bi);
+    argmax_row_step<DPP_QUAD_XOR2>(bv, bi);
+    argmax_row_step<DPP_ROW_HALF_MIRROR>(bv, bi);
+    argmax_row_step<DPP_ROW_MIRROR>(bv, bi);
+    // every lane of a 16-lane row holds the row's winner; the four rows meet in uniform registers
+    float wv = readlane_f(bv, 0);
+    int wi = __builtin_amdgcn_readlane(bi, 0);
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      if (beats(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
+    for (int r = 16; r < 64; r += 16) {
+      const float rv = readlane_f(bv, r);
+      const int ri = __builtin_amdgcn_readlane(bi, r);
+      if (beats(rv, ri, wv, wi)) {
+        wv = rv;
+        wi = ri;
       }
+    }
+    const int ce = min(wi, E - 1);  // stays in range even for NaN scores
+    float held = 0.f;
+#pragma unroll
+    for (int p = 0; p < SEL_MAX_P; ++p)
+      if (p == (ce >> 6)) held = sraw[p];
+    const float s_win = readlane_f(held, ce & 63);
+    sum = __fadd_rn(sum, s_win);
+    if (lane == slot) {
+      my_e = ce;
+      my_s = s_win;
     }
 #pragma unroll
     for (int p = 0; p < SEL_MAX_P; ++p)
-      if (lane + 64 * p == bi) elig[p] = false;  // k <= eligible count is checked on the host
-    if (lane == 0) chosen[wave][slot] = min(bi, E - 1);  // stays in range even for NaN scores
+      if (lane + 64 * p == wi) elig[p] = false;  // k <= eligible count is checked on the host
   }
-  __syncthreads();
 
   if (live && lane < k) {
-    const int e = chosen[wave][lane];
-    const float s_mine = s_raw[wave][e];
     float w;
     if (norm) {
-      float sum = 0.f;
-      for (int j = 0; j < k; ++j) sum = __fadd_rn(sum, s_raw[wave][chosen[wave][j]]);
       const float den = __fadd_rn(sum, eps);
-      w = __fmul_rn(alpha, __fdiv_rn(s_mine, den));
+      w = __fmul_rn(alpha, __fdiv_rn(my_s, den));
     } else {
-      w = __fmul_rn(alpha, s_mine);
+      w = __fmul_rn(alpha, my_s);
     }
-    idx_out[n * k + lane] = e;
+    idx_out[n * k + lane] = my_e;
     w_out[n * k + lane] = w;
   }
 }
@@ -429,6 +527,12 @@ int router_rows_per_block(int dtype) { return dtype == MOE_BF16 ? RB_BM : LG_BM;
 RouterPlan router_plan(int dtype, int64_t N, int D, int E) {
   RouterPlan p;
   p.split = dtype == MOE_BF16;
+  p.gemv = p.split && N >= 1 && N <= RG_MAX_N;
+  if (p.gemv) {
+    p.ks = 1;
+    p.kchunk = D;
+    return p;
+  }
   const int64_t bm = p.split ? RB_BM : LG_BM, bn = p.split ? 32 * router_nj(N, E) : LG_BN;
   int64_t tiles = ((N + bm - 1) / bm) * ((E + bn - 1) / bn);
   if (tiles < 1) tiles = 1;  // N = 0
@@ -452,6 +556,18 @@ hipError_t launch_router_split(const float* wg, int E, int D, uint16_t* w3, hipS
 
 hipError_t launch_logits(int dtype, const RouterPlan& p, const void* x, const float* wg, const uint16_t* w3, int64_t N,
                          int D, int E, float* part, hipStream_t s) {
+  if (p.gemv) {
+    auto go = [&](auto kernel) {
+      hipLaunchKernelGGL(kernel, dim3((unsigned)E), dim3(64), 0, s, (const uint16_t*)x, w3, D, E, part);
+    };
+    switch (N) {
+      case 1: go(logits_gemv_kernel<1>); break;
+      case 2: go(logits_gemv_kernel<2>); break;
+      case 3: go(logits_gemv_kernel<3>); break;
+      default: go(logits_gemv_kernel<4>); break;
+    }
+    return hipGetLastError();
+  }
   if (p.split) {
     const int nj = router_nj(N, E);
     const int64_t blocks = (N + RB_BM - 1) / RB_BM * ((E + 32 * nj - 1) / (32 * nj)) * p.ks;

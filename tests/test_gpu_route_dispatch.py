@@ -119,12 +119,18 @@ def test_scores_within_bound(name):
 
 # Router GEMM tile shapes: E past 256 and not a multiple of 32 (two blocks of five 32-expert tiles, the
 # last partly past E), E = 100 (four tiles, the last partly past E), batches of one token block and of
-# one partial block (two tiles per block), token counts that leave a partial 128-token block.
+# one partial block (two tiles per block), token counts that leave a partial 128-token block; and
+# batches of one to four tokens (the one-wave-per-expert kernel), among them D = 64 (fewer 8-element
+# chunks than lanes), E = 512 and the GLM-5 router's D = 6144.
 GEMM_SHAPES = [
     dict(N=777, D=256, E=300, k=8),
     dict(N=260, D=512, E=100, k=6),
     dict(N=5, D=320, E=40, k=4),
     dict(N=128, D=192, E=96, k=2),
+    dict(N=1, D=6144, E=256, k=8),
+    dict(N=2, D=5120, E=160, k=8),
+    dict(N=3, D=320, E=40, k=4),
+    dict(N=4, D=64, E=512, k=8),
 ]
 
 
