@@ -145,7 +145,8 @@ moe_status moe_router_prepare(const moe_config* cfg, const float* w_router, void
  *   workspace, ws_bytes: scratch of at least moe_workspace_size(cfg, N) bytes (unused, may be NULL,
  *            with MOE_ROUTE_SCORES_IN)
  * The logits are float32 dot products (bf16 activations: exact products of x with an exact three-piece
- * bf16 split of w_router, accumulated in float32 on the matrix cores). Given the same float32 scores,
+ * bf16 split of w_router, accumulated in float32: on the matrix cores, or with fused multiply-adds for
+ * batches of one to four tokens). Given the same float32 scores,
  * indices and weights are bit-identical to a float32 evaluation in the order stated above (correctly
  * rounded add, divide and multiply). */
 moe_status moe_route(const moe_config* cfg, int64_t N, const void* x, const void* w_router, const float* e_bias,

@@ -9,7 +9,8 @@
 //  - bf16 activations: the float32 router weight is split exactly into three bf16 pieces,
 //    W = hi + mid + lo (each piece the bf16 rounding of what the previous ones left), so every product
 //    x * piece is exact in float32 and the bf16 matrix cores accumulate x W in float32 at 3x the bf16
-//    work instead of running the 16x slower float32 matrix path.
+//    work instead of running the 16x slower float32 matrix path; batches of one to four tokens take a
+//    one-wave-per-expert kernel that adds the same exact products with fused multiply-adds.
 //  - float32 activations: v_mfma_f32_16x16x4_f32 (exact float32 products, float32 accumulation).
 #include <hip/hip_runtime.h>
 
