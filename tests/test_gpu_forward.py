@@ -121,13 +121,15 @@ def test_forward_deterministic_and_permutation_equivariant():
     assert np.array_equal(y3, y1[perm]) and np.array_equal(i3, i1[perm]) and np.array_equal(w3, w1[perm])
 
 
-@pytest.mark.parametrize("name", ["glm5_decode", "air_prefill"])
-def test_forward_prepared_router_bitexact(name):
+@pytest.mark.parametrize("name,tokens", [("glm5_decode", None), ("air_prefill", None), ("glm5_decode", 1)])
+def test_forward_prepared_router_bitexact(name, tokens):
     """The forward on moe_router_prepare's output (the split taken once) equals the forward that splits
-    the float32 router weight itself, bit for bit."""
+    the float32 router weight itself, bit for bit (one token: the small-batch gate kernel)."""
     import sparse_moe_layer_gate_amd as moe
 
     w = synth.WORKLOADS[name]
+    if tokens is not None:
+        w = w.with_tokens(tokens)
     _, _, dev = H.device_weights(w, generate_on_device=True)
     x_dev = H.to_device(synth.x_host(w))
     y1, i1, w1, c1 = H.gpu_forward(w, x_dev, dev)

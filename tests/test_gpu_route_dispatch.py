@@ -215,16 +215,19 @@ def test_dispatch_own_workspace(N):
         assert np.array_equal(H.to_host(g), r), what
 
 
-@pytest.mark.parametrize("name", ["glm5_decode", "air_prefill"])
-def test_route_prepared_and_without_scores(name):
+@pytest.mark.parametrize("name,tokens", [("glm5_decode", None), ("air_prefill", None), ("glm5_decode", 1),
+                                         ("glm5_decode", 3)])
+def test_route_prepared_and_without_scores(name, tokens):
     """moe_route on the prepared router weight (moe_router_prepare) gives the same scores, ids and weights,
     bit for bit, as on the float32 weight; without MOE_ROUTE_SCORES_OUT the ids and weights are the same
-    and no scores are needed."""
+    and no scores are needed. One and three tokens run the small-batch gate kernel."""
     import torch
 
     import sparse_moe_layer_gate_amd as moe
 
     w = synth.WORKLOADS[name]
+    if tokens is not None:
+        w = w.with_tokens(tokens)
     x = synth.x_host(w)
     wg, b = synth.router_host(w)
     cfg = moe.config_of(w)
