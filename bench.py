@@ -69,8 +69,8 @@ def read_traffic(workload: str) -> dict | None:
 
 
 KERNEL_NAMES = {  # library stage -> substrings of the HIP kernel symbols that run it (first match wins)
-    "experts_gate_up": [("grouped_bf16_w8<true>", ""), ("grouped_bf16_lds<", "true>")],
-    "experts_down": [("grouped_bf16_w8<false>", ""), ("grouped_bf16_lds<", "false>")],
+    "experts_gate_up": [("grouped_bf16_w8<true>", "")],
+    "experts_down": [("grouped_bf16_w8<false>", "")],
     "experts_gate_up_decode": [("grouped_bf16_decode<true", "")],
     "experts_down_decode": [("grouped_bf16_decode<false", "")],
 }

@@ -285,12 +285,6 @@ __global__ __launch_bounds__(256) void dense_tiles_kernel(int64_t N, TileSpec t0
   }
 }
 
-__global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* __restrict__ p, int64_t n, int32_t v) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = v;
-}
-
-}  // namespace
-
 __global__ __launch_bounds__(256) void fill2_i32_kernel(int32_t* __restrict__ p, int64_t n, int32_t* __restrict__ q,
                                                        int64_t m, int32_t v) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n + m; i += (int64_t)gridDim.x * 256) {
@@ -301,17 +295,12 @@ __global__ __launch_bounds__(256) void fill2_i32_kernel(int32_t* __restrict__ p,
   }
 }
 
+}  // namespace
+
 hipError_t launch_fill2_i32(int32_t* p, int64_t n, int32_t* q, int64_t m, int32_t v, hipStream_t s) {
   if (n + m <= 0) return hipSuccess;
   const int64_t blocks = min((n + m + 255) / 256, (int64_t)1024);
   hipLaunchKernelGGL(fill2_i32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n, q, m, v);
-  return hipGetLastError();
-}
-
-hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  const int64_t blocks = min((n + 255) / 256, (int64_t)1024);
-  hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n, v);
   return hipGetLastError();
 }
 

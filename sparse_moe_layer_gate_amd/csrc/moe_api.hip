@@ -294,7 +294,6 @@ moe_status experts_impl(const moe_config* cfg, int64_t N, const void* x, const m
   g.sorted_pair = at<int32_t>(ws, L.sorted_pair);
   g.topk_w = w;
   g.k = k;
-  g.offsets = at<int32_t>(ws, L.offsets);
   g.swiglu_limit = cfg->swiglu_limit;
   g.gather_rows = N;
   // gate_up + SwiGLU: routed rows gather x through sorted_pair; the shared expert reads x in order
@@ -566,8 +565,7 @@ moe_status moe_dense_forward(int64_t N, int32_t D, int32_t dff, int32_t dtype, f
   TileSpec t0{L.bm, at<Tile>(ws, L.tiles0), ntiles, 0, ntiles + 2};
   TileSpec t1{L.bm, at<Tile>(ws, L.tiles1), ntiles + 1, 0, ntiles + 10};
   if (launch_dense_tiles(N, t0, t1, s) != hipSuccess) return MOE_ERR_HIP;
-  // one dense problem through the grouped GEMMs: no gather, no row scale; offsets = nullptr marks it
-  // as a large problem for the prefill kernel's loop choice
+  // one dense problem through the grouped GEMMs: no gather, no row scale
   GroupedArgs g{};
   g.k = 1;
   g.swiglu_limit = swiglu_limit;

@@ -133,7 +133,6 @@ struct GroupedArgs {
   const int32_t* sorted_pair;
   const float* topk_w;
   int k;
-  const int32_t* offsets;  // routed experts' row offsets [E + 1] (or nullptr: every expert counts as large)
   float swiglu_limit;      // gate_up epilogue clamp bound (0: plain SwiGLU)
   int64_t gather_rows;     // rows of the matrix that gathered A rows index (x); 0 when unknown
   int32_t* work_ctr;       // 8 counters, zero at launch: per-XCD work claims of the persistent kernels
@@ -186,9 +185,8 @@ hipError_t launch_bf16_decode(bool gate_up, const GroupedArgs& a, int64_t max_ti
 // y = alpha_out * (routed rows in slot order) + shared row
 hipError_t launch_combine(int dtype, const void* Y, const void* Ysh, const int32_t* inv_row, int64_t N, int k, int D,
                           float alpha_out, void* y, hipStream_t s);
-// p[0 .. n) = v (a kernel rather than a memset node, so the call may sit in a captured graph)
-hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
-// p[0 .. n) = v and q[0 .. m) = v in one launch
+// p[0 .. n) = v and q[0 .. m) = v in one launch (a kernel rather than memset nodes, so the call may sit
+// in a captured graph)
 hipError_t launch_fill2_i32(int32_t* p, int64_t n, int32_t* q, int64_t m, int32_t v, hipStream_t s);
 
 }  // namespace moe
