@@ -99,6 +99,8 @@ def profile_summary(pdir: str, workload: str, decode: bool) -> str:
          FETCH_SIZE_copy/, WRITE_SIZE_copy/   the same counters on `bench.py --copy-calibration`
          MFMA/         rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_INSTS_MFMA
                        TCC_HIT_sum TCC_MISS_sum (optional)
+         LOADS/        rocprofv3 --pmc GRBM_GUI_ACTIVE TA_TA_BUSY TA_BUFFER_READ_LDS_WAVEFRONTS
+                       SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_VMEM_RD (optional)
        Byte counters are scaled by bytes-copied / counter-reading of the 1 GiB copy; with them, also writes
        the dominant kernel's traffic file read by the benchmark."""
     stats = _csv_rows(_find(os.path.join(pdir, "trace"), "_kernel_stats.csv"))
@@ -174,6 +176,36 @@ def profile_summary(pdir: str, workload: str, decode: bool) -> str:
                                                           sum(c.get("TCC_MISS_sum", [0.0])))
             lines.append(f"| `{k[:70]}` | {ns / 1e6:.4f} | {ghz:.3f} | {busy:.1%} | "
                          f"{busy * ghz / 2.4 * P_BF16 / 1e12:.0f} | {hit:.1%} |")
+
+    if os.path.isdir(os.path.join(pdir, "LOADS")):
+        rows = _csv_rows(_find(os.path.join(pdir, "LOADS"), "_counter_collection.csv"))
+        acc, dur = {}, {}
+        for r in rows:
+            k = r["Kernel_Name"]
+            acc.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            dur.setdefault(k, set()).add((r["Dispatch_Id"], int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+        lines += ["", "## Direct loads and LDS (rocprofv3 --pmc, one pass)", "",
+                  "Each load-to-LDS wavefront moves 64 lanes x 16 bytes: L2 -> LDS bytes = 1 KiB x "
+                  "(TA_BUFFER_READ_LDS_WAVEFRONTS + TA_FLAT_READ_LDS_WAVEFRONTS), per CU and clock over the "
+                  "kernel's cycles (GRBM_GUI_ACTIVE / 8) and 256 CUs. TA busy = TA_TA_BUSY / (cycles x 256). "
+                  "LDS bank conflicts = SQ_LDS_BANK_CONFLICT / (SQ_LDS_IDX_ACTIVE - SQ_LDS_BANK_CONFLICT), "
+                  "conflict cycles per conflict-free LDS cycle.", "",
+                  "| kernel | avg ms (under counters) | L2 -> LDS GB | B / clock / CU | TA busy | LDS bank conflicts |",
+                  "|---|---:|---:|---:|---:|---:|"]
+        for k, c in acc.items():
+            waves = sum(c.get("TA_BUFFER_READ_LDS_WAVEFRONTS", [0.0])) + sum(c.get("TA_FLAT_READ_LDS_WAVEFRONTS",
+                                                                                    [0.0]))
+            if waves == 0:
+                continue
+            n = len(c["GRBM_GUI_ACTIVE"])
+            cyc = sum(c["GRBM_GUI_ACTIVE"]) / n / 8
+            ns = sum(d for _, d in dur[k]) / len(dur[k])
+            nbytes = waves / n * 1024.0
+            ta = sum(c.get("TA_TA_BUSY", [0.0])) / n / (cyc * 256)
+            conf = sum(c.get("SQ_LDS_BANK_CONFLICT", [0.0])) / n
+            idx = sum(c.get("SQ_LDS_IDX_ACTIVE", [0.0])) / n
+            lines.append(f"| `{k[:70]}` | {ns / 1e6:.4f} | {nbytes / 1e9:.2f} | {nbytes / (cyc * 256):.1f} | "
+                         f"{ta:.1%} | {conf / max(1.0, idx - conf):.3f} |")
     return "\n".join(lines) + "\n"
 
 
