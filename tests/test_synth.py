@@ -73,3 +73,21 @@ def test_workload_shapes():
     off = wg - plain
     assert np.allclose(off, off[:, :1], atol=1e-6)  # one offset per router row
     assert 0.2 < off[:, 0].std() < 0.8
+
+
+def test_skew_workloads_saturation_and_load():
+    """The two GLM-4.5 prefill recipes on their first 1,024 tokens: offsets of std 0.5 saturate a share of
+    the sigmoid scores and pile the rows on a few experts; offsets of std 0.02 saturate none and still
+    load the experts unevenly (largest well above the mean)."""
+    import oracle
+
+    for name, saturated, skewed in [("glm45_prefill_skewed", True, 6.0), ("glm45_prefill_mild_skew", False, 3.0)]:
+        w = synth.WORKLOADS[name].with_tokens(1024)
+        x = synth.x_host(w)
+        wg, b = synth.router_host(w)
+        s = oracle.scores(w, x, wg)
+        sat = float(np.mean(s == np.float32(1.0)))
+        idx, _ = oracle.select(w, s, b)
+        load = np.bincount(idx.ravel(), minlength=w.E)
+        assert (sat > 0.05) if saturated else (sat == 0.0), (name, sat)
+        assert load.max() > skewed * load.mean(), (name, load.max(), load.mean())
