@@ -85,6 +85,15 @@ struct Wave8Tile {
   }
 };
 
+template <bool V>
+struct BoolC {
+  static constexpr bool value = V;
+};
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+
 // Word 3 of a raw (untyped, stride 0) buffer descriptor on gfx9-family parts: 32-bit data format, no
 // swizzle, no index stride.
 constexpr int kRawBufferWord3 = 0x00020000;
@@ -169,25 +178,32 @@ __device__ __attribute__((always_inline)) inline void wave8_loop(char* lds, __am
     wait_vmcnt<0>();
   }
   bare_barrier();
-  for (int kt = 0; kt < nk; ++kt) {
+  // The steps that issue both operands' loads run in a loop of their own, free of the branches and of
+  // the variable waits of the last two steps, which are peeled (with the small-tile loop peeled the same
+  // way, against one loop with the conditions inside: dense FFN gate_up 1.74 -> 1.65 ms, skewed GLM-4.5
+  // layer 4.22 -> 4.08 ms, Air 1.75 -> 1.63 ms; 239 -> 207 VGPRs in gate_up).
+  auto step = [&](int kt, auto more_a, auto more_b) {
+    constexpr bool MA = decltype(more_a)::value, MB = decltype(more_b)::value;
     // step kt is in LDS: A stage kt % 2, B stage kt % 3
-    if (kt + 1 < nk) issue_a(kt + 1);  // into the A stage step kt - 1 used (every wave is done with it)
+    if (MA) issue_a(kt + 1);  // into the A stage step kt - 1 used (every wave is done with it)
     read_frags(kt, 0);
     wait_lgkm0();
-    read_frags(kt, 1);                 // lands while the lo half's MFMAs run
+    read_frags(kt, 1);        // lands while the lo half's MFMAs run
     compute(0);
-    if (kt + 2 < nk) issue_b(kt + 2);  // into the B stage step kt - 1 used
+    if (MB) issue_b(kt + 2);  // into the B stage step kt - 1 used
     wait_lgkm0();
     compute(1);
     // step kt + 1 has landed (only this wave's B loads of step kt + 2 may still be in flight)
-    if (kt + 1 < nk) {
-      if (kt + 2 < nk)
-        wait_vmcnt<NL>();
-      else
-        wait_vmcnt<0>();
-    }
+    if (MB)
+      wait_vmcnt<NL>();
+    else if (MA)
+      wait_vmcnt<0>();
     bare_barrier();
-  }
+  };
+  int kt = 0;
+  for (; kt + 2 < nk; ++kt) step(kt, BoolC<true>{}, BoolC<true>{});
+  if (kt + 1 < nk) step(kt++, BoolC<true>{}, BoolC<false>{});
+  step(kt, BoolC<false>{}, BoolC<false>{});
 }
 
 // The K loop of one wave for a tile of at most 64 valid rows. Such a block is a stream of its expert's
@@ -266,8 +282,11 @@ __device__ __attribute__((always_inline)) inline void wave8_loop_small(char* lds
   else
     wait_vmcnt<0>();
   bare_barrier();
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 3 < nk) issue(kt + 3);  // into the stage step kt - 1 used (every wave is done with it)
+  // AHEAD: steps issued after step kt + 1 when step kt ends (2 in the main loop, then 1, 0); the last
+  // step waits for nothing. As in the large-tile loop, the main steps run in a loop of their own.
+  auto step = [&](int kt, auto ahead_tag) {
+    constexpr int AHEAD = decltype(ahead_tag)::value;
+    if (AHEAD == 2) issue(kt + 3);  // into the stage step kt - 1 used (every wave is done with it)
     read_frags(kt, 0);
     wait_lgkm0();
     read_frags(kt, 1);
@@ -275,16 +294,19 @@ __device__ __attribute__((always_inline)) inline void wave8_loop_small(char* lds
     wait_lgkm0();
     compute(1);
     // step kt + 1 has landed (steps kt + 2 and kt + 3 may still be in flight)
-    if (kt + 1 < nk) {
-      if (kt + 3 < nk)
-        wait_vmcnt<2 * PER>();
-      else if (kt + 2 < nk)
-        wait_vmcnt<PER>();
-      else
-        wait_vmcnt<0>();
-    }
+    if (AHEAD == 2)
+      wait_vmcnt<2 * PER>();
+    else if (AHEAD == 1)
+      wait_vmcnt<PER>();
+    else if (AHEAD == 0)
+      wait_vmcnt<0>();
     bare_barrier();
-  }
+  };
+  int kt = 0;
+  for (; kt + 3 < nk; ++kt) step(kt, IntC<2>{});
+  if (kt + 2 < nk) step(kt++, IntC<1>{});
+  if (kt + 1 < nk) step(kt++, IntC<0>{});
+  step(kt, IntC<-1>{});
 }
 
 // One logical block of the eight-wave kernel: row tile and column tile from the logical id L, K loop,
