@@ -97,7 +97,6 @@ struct IntC {
 // Word 3 of a raw (untyped, stride 0) buffer descriptor on gfx9-family parts: 32-bit data format, no
 // swizzle, no index stride.
 constexpr int kRawBufferWord3 = 0x00020000;
-constexpr uint32_t kNoRow = 0xffffffffu;  // marks a direct-load lane that loads nothing
 
 // s_waitcnt lgkmcnt(0), other counters at their maximum
 __device__ inline void wait_lgkm0() { __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8)); }
@@ -110,13 +109,15 @@ __device__ inline void bare_barrier() {
 }
 
 // The K loop of one wave. offA / offB: byte offsets of this wave's direct-load sources in its half's
-// rows (A lanes of rows past the tile's valid rows load nothing; B is never skipped, so a wave's newest
-// NL loads are always B loads, which is what the vmcnt(NL) waits rely on).
+// rows; na: how many of its A loads reach a valid row (the others are not issued; lanes of an issued
+// load past the tile repeat its last row). B is never skipped, so a wave's newest NL loads are always
+// B loads, which is what the vmcnt(NL) waits rely on.
 template <bool GATE_UP, int MI>
 __device__ __attribute__((always_inline)) inline void wave8_loop(char* lds, __amdgpu_buffer_rsrc_t rsrcA,
-                                                                 const uint32_t (&offA)[4], __amdgpu_buffer_rsrc_t rsrcB,
-                                                                 const uint32_t (&offB)[4], f32x16 (&acc)[2][4], int nk,
-                                                                 int grp, int q, int lane, int m0, int wn) {
+                                                                 const uint32_t (&offA)[4], int na,
+                                                                 __amdgpu_buffer_rsrc_t rsrcB, const uint32_t (&offB)[4],
+                                                                 f32x16 (&acc)[2][4], int nk, int grp, int q, int lane,
+                                                                 int m0, int wn) {
   using T = Wave8Tile<GATE_UP>;
   constexpr int NL = T::NL, TN = 4, ROWB = T::ROWB;
   const int sw = T::swz(lane & 31);
@@ -134,7 +135,7 @@ __device__ __attribute__((always_inline)) inline void wave8_loop(char* lds, __am
     char* dst = lds + (kstep % T::A_STAGES) * T::OPB + half_off;
 #pragma unroll
     for (int i = 0; i < NL; ++i)
-      if (offA[i] != kNoRow)
+      if (i < na)  // wave-uniform: loads wholly past the tile's rows are not issued
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrcA, (lds_void*)(dst + i * 4096), 16, (int)offA[i], kstep * T::BK * 2,
                                                  0, 0);
   };
@@ -363,13 +364,12 @@ __device__ __forceinline__ void w8_block(const GroupedArgs& a, int ncol_max, int
     const int r = grp * 128 + (p >> 3), c = (p & 7) ^ T::swz(r);
     const int col = min(col0 + (GATE_UP ? r % (T::BN / 2) : r), P.ncols - 1);
     offB[i] = ((uint32_t)col * (uint32_t)P.K + 8 * c) * 2;
-    if (r < tile.rows) {
-      const int64_t g = P.gather ? a.sorted_pair[(int64_t)tile.row_start + r] / a.k : r;
-      offA[i] = (uint32_t)(g * P.lda + 8 * c) * 2;
-    } else {
-      offA[i] = kNoRow;  // past the tile's valid rows: not loaded
-    }
+    const int rr = min(r, tile.rows - 1);  // rows past the tile repeat its last row (never stored)
+    const int64_t g = P.gather ? a.sorted_pair[(int64_t)tile.row_start + rr] / a.k : rr;
+    offA[i] = (uint32_t)(g * P.lda + 8 * c) * 2;
   }
+  // A loads of this wave that reach a valid row: load i covers rows 128 g + 32 i + 8 q + [0, 8)
+  const int na = max(0, min(NL, (tile.rows - grp * 128 - 8 * q + 31) / 32));
   // small ring: this lane's A chunk is row 8 wave + lane / 8 (past the tile: its last row), slot lane % 8
   uint32_t offA1 = 0;
   if (small) {
@@ -399,11 +399,11 @@ __device__ __forceinline__ void w8_block(const GroupedArgs& a, int ncol_max, int
     else
       wave8_loop_small<GATE_UP, 0>(lds, rsrcA, offA1, rsrcB, offB, acc, nk, grp, q, wave, lane, m0, wn);
   } else if (mi == 2) {
-    wave8_loop<GATE_UP, 2>(lds, rsrcA, offA, rsrcB, offB, acc, nk, grp, q, lane, m0, wn);
+    wave8_loop<GATE_UP, 2>(lds, rsrcA, offA, na, rsrcB, offB, acc, nk, grp, q, lane, m0, wn);
   } else if (mi == 1) {
-    wave8_loop<GATE_UP, 1>(lds, rsrcA, offA, rsrcB, offB, acc, nk, grp, q, lane, m0, wn);
+    wave8_loop<GATE_UP, 1>(lds, rsrcA, offA, na, rsrcB, offB, acc, nk, grp, q, lane, m0, wn);
   } else {
-    wave8_loop<GATE_UP, 0>(lds, rsrcA, offA, rsrcB, offB, acc, nk, grp, q, lane, m0, wn);
+    wave8_loop<GATE_UP, 0>(lds, rsrcA, offA, na, rsrcB, offB, acc, nk, grp, q, lane, m0, wn);
   }
 
   // Epilogue through LDS (the loop ended on a barrier after the last operand read): each wave stages
