@@ -65,15 +65,20 @@ __device__ void build_tiles(const TileSpec& ts, bool valid, int e, int cnt, int 
                             int n_shared_problem, int* wsum) {
   const int nt = valid ? (cnt + ts.bm - 1) / ts.bm : 0;
   const bool small = valid && cnt >= 1 && cnt <= ts.small_max && cnt <= ts.bm;
+  // list slots of a large expert: its tiles, padded with empty ones (rows 0) to a multiple of
+  // MOE_TILE_ALIGN in the 256-row lists, so that an expert's tiles start a rasterization row group
+  const int align = (ts.small_max > 0 && MOE_TILE_ALIGN > 1) ? MOE_TILE_ALIGN : 1;
+  const int slots = small ? 0 : (nt + align - 1) / align * align;
   int na, nrouted;
   const int ia = block_exclusive_scan(small ? 1 : 0, wsum, &na);
-  const int ib = block_exclusive_scan(small ? 0 : nt, wsum, &nrouted);
+  const int ib = block_exclusive_scan(slots, wsum, &nrouted);
   const int nsh = n_shared_problem ? (int)((N + ts.bm - 1) / ts.bm) : 0;
   const int nb = nrouted + nsh;
   if (small) {
     ts.tiles[nb + ia] = Tile{0, e, off, cnt};
   } else {
     for (int j = 0; j < nt; ++j) ts.tiles[ib + j] = Tile{0, e, off + j * ts.bm, min(ts.bm, cnt - j * ts.bm)};
+    for (int j = nt; j < slots; ++j) ts.tiles[ib + j] = Tile{0, e, off, 0};
   }
   for (int j = threadIdx.x; j < nsh; j += blockDim.x)
     ts.tiles[nrouted + j] = Tile{1, 0, j * ts.bm, (int)min((int64_t)ts.bm, N - (int64_t)j * ts.bm)};

@@ -133,7 +133,9 @@ hipError_t launch_grouped(Kern kern, const GroupedArgs& a, int64_t max_tile_coun
 
 int64_t max_tiles(int64_t N, int k, int E, int n_shared_problem, int bm) {
   const int64_t pairs = N * k;
-  const int64_t routed = pairs / bm + (pairs < E ? pairs : E);
+  int64_t routed = pairs / bm + (pairs < E ? pairs : E);
+  // padding of the 256-row lists (MOE_TILE_ALIGN): at most MOE_TILE_ALIGN - 1 empty tiles per expert
+  if (bm == 256 && MOE_TILE_ALIGN > 1) routed += (int64_t)(MOE_TILE_ALIGN - 1) * (pairs < E ? pairs : E);
   const int64_t shared = n_shared_problem ? (N + bm - 1) / bm : 0;
   return routed + shared;
 }
@@ -187,7 +189,8 @@ int tile_plan_rows(int i) { return i == 0 ? MOE_DECODE_ROWS : MOE_PICK_BAND_ROWS
 // of the prefill kernels hold the large experts' tiles together. (An earlier order merged them evenly
 // among the others to balance the XCDs' runs before the kernels claimed work per XCD; with the claiming
 // kernels and 2 x 16 rectangles the separated order is 2-4% faster on GLM-5 and Air and equal on the
-// skewed GLM-4.5 layer.)
+// skewed GLM-4.5 layer.) Each large expert's tiles are padded to an even number of list slots
+// (MOE_TILE_ALIGN), so that its tiles share a rectangle.
 int small_expert_rows(int dtype, int bm) { return (dtype == MOE_BF16 && bm == 256) ? MOE_SMALL_EXPERT_ROWS : 0; }
 
 hipError_t launch_gate_up(int dtype, const GroupedArgs& a, int64_t max_tile_count, hipStream_t s) {

@@ -333,6 +333,7 @@ __device__ __forceinline__ void w8_block(const GroupedArgs& a, int ncol_max, int
   const int64_t tile_id = sg * GR + w2 % gr;
   const int ct = (int)(cg * GC + w2 / gr);
   const Tile tile = a.tiles[tile_id];
+  if (tile.rows <= 0) return;  // padding
   const ExpertProblem P = pick_problem(a, tile.problem);
   const int col0 = ct * T::COLS;
   if (col0 >= P.ncols) return;
