@@ -66,23 +66,32 @@ __device__ void build_tiles(const TileSpec& ts, bool valid, int e, int cnt, int 
   const int nt = valid ? (cnt + ts.bm - 1) / ts.bm : 0;
   const bool small = valid && cnt >= 1 && cnt <= ts.small_max && cnt <= ts.bm;
   // list slots of a large expert: its tiles, padded with empty ones (rows 0) to a multiple of
-  // MOE_TILE_ALIGN in the 256-row lists, so that an expert's tiles start a rasterization row group
-  const int align = (ts.small_max > 0 && MOE_TILE_ALIGN > 1) ? MOE_TILE_ALIGN : 1;
+  // MOE_TILE_ALIGN in the 256-row lists, so that an expert's tiles start a rasterization row group;
+  // hot experts (MOE_HOT_TILES tiles or more) come first, padded to MOE_HOT_ALIGN
+  const bool lists256 = ts.small_max > 0;
+  const bool hot = lists256 && MOE_HOT_TILES > 0 && !small && nt >= MOE_HOT_TILES;
+  const int align = hot ? MOE_HOT_ALIGN : (lists256 && MOE_TILE_ALIGN > 1) ? MOE_TILE_ALIGN : 1;
   const int slots = small ? 0 : (nt + align - 1) / align * align;
-  int na, nrouted;
+  int na, nhot, nrest;
   const int ia = block_exclusive_scan(small ? 1 : 0, wsum, &na);
-  const int ib = block_exclusive_scan(slots, wsum, &nrouted);
+  const int ih = block_exclusive_scan(hot ? slots : 0, wsum, &nhot);
+  const int ir = block_exclusive_scan(hot ? 0 : slots, wsum, &nrest);
+  const int nrouted = nhot + nrest;
   const int nsh = n_shared_problem ? (int)((N + ts.bm - 1) / ts.bm) : 0;
   const int nb = nrouted + nsh;
   if (small) {
     ts.tiles[nb + ia] = Tile{0, e, off, cnt};
   } else {
+    const int ib = hot ? ih : nhot + ir;
     for (int j = 0; j < nt; ++j) ts.tiles[ib + j] = Tile{0, e, off + j * ts.bm, min(ts.bm, cnt - j * ts.bm)};
     for (int j = nt; j < slots; ++j) ts.tiles[ib + j] = Tile{0, e, off, 0};
   }
   for (int j = threadIdx.x; j < nsh; j += blockDim.x)
     ts.tiles[nrouted + j] = Tile{1, 0, j * ts.bm, (int)min((int64_t)ts.bm, N - (int64_t)j * ts.bm)};
-  if (threadIdx.x == 0) *ts.n_tiles = na + nb;
+  if (threadIdx.x == 0) {
+    *ts.n_tiles = na + nb;
+    if (ts.n_hot) *ts.n_hot = nhot;
+  }
   if (ts.work_ctr && threadIdx.x < 8) ts.work_ctr[threadIdx.x] = 0;
 }
 
@@ -285,7 +294,10 @@ __global__ __launch_bounds__(256) void dense_tiles_kernel(int64_t N, TileSpec t0
       t.rows = (int)min((int64_t)ts.bm, N - j * ts.bm);
       ts.tiles[j] = t;
     }
-    if (blockIdx.x == 0 && threadIdx.x == 0) *ts.n_tiles = (int)nt;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      *ts.n_tiles = (int)nt;
+      if (ts.n_hot) *ts.n_hot = 0;
+    }
     if (blockIdx.x == 0 && threadIdx.x < 8 && ts.work_ctr) ts.work_ctr[threadIdx.x] = 0;
   }
 }

@@ -134,8 +134,10 @@ hipError_t launch_grouped(Kern kern, const GroupedArgs& a, int64_t max_tile_coun
 int64_t max_tiles(int64_t N, int k, int E, int n_shared_problem, int bm) {
   const int64_t pairs = N * k;
   int64_t routed = pairs / bm + (pairs < E ? pairs : E);
-  // padding of the 256-row lists (MOE_TILE_ALIGN): at most MOE_TILE_ALIGN - 1 empty tiles per expert
-  if (bm == 256 && MOE_TILE_ALIGN > 1) routed += (int64_t)(MOE_TILE_ALIGN - 1) * (pairs < E ? pairs : E);
+  // padding of the 256-row lists (MOE_TILE_ALIGN, MOE_HOT_ALIGN): at most that many empty tiles less one
+  // per expert
+  const int pad = (MOE_HOT_TILES > 0 && MOE_HOT_ALIGN > MOE_TILE_ALIGN) ? MOE_HOT_ALIGN : MOE_TILE_ALIGN;
+  if (bm == 256 && pad > 1) routed += (int64_t)(pad - 1) * (pairs < E ? pairs : E);
   const int64_t shared = n_shared_problem ? (N + bm - 1) / bm : 0;
   return routed + shared;
 }

@@ -312,8 +312,21 @@ __device__ __attribute__((always_inline)) inline void wave8_loop_small(char* lds
 
 // One logical block of the eight-wave kernel: row tile and column tile from the logical id L, K loop,
 // epilogue. Every wave of the block calls it with the same arguments.
+// Logical block L of a region of n_region row tiles -> (row tile within the region, column tile): walk
+// rectangles of GR row tiles x GC column tiles (the last ones of a row group or of the region smaller),
+// row tiles fastest.
+template <int GR, int GC>
+__device__ inline void raster(int64_t L, int ncol_max, int64_t n_region, int64_t& tile_rel, int& ct) {
+  const int64_t sg = L / ((int64_t)GR * ncol_max), within = L % ((int64_t)GR * ncol_max);
+  const int64_t gr = min((int64_t)GR, n_region - sg * GR);
+  const int64_t cg = within / (gr * GC), w2 = within % (gr * GC);
+  tile_rel = sg * GR + w2 % gr;
+  ct = (int)(cg * GC + w2 / gr);
+}
+
 template <bool GATE_UP>
-__device__ __forceinline__ void w8_block(const GroupedArgs& a, int ncol_max, int64_t n_tiles, int64_t L, char* lds) {
+__device__ __forceinline__ void w8_block(const GroupedArgs& a, int ncol_max, int64_t n_tiles, int64_t n_hot, int64_t L,
+                                         char* lds) {
   using T = Wave8Tile<GATE_UP>;
   constexpr int NL = T::NL, OC = T::OC;
   constexpr int OPITCH = OC + 8;  // bf16 per staged output row (16-byte pad)
@@ -321,17 +334,25 @@ __device__ __forceinline__ void w8_block(const GroupedArgs& a, int ncol_max, int
   constexpr int WROW_OFF = OUT_BYTES;  // row scales (down), after the staged outputs
   static_assert(T::RING <= 160 * 1024 && WROW_OFF + 256 * 4 <= T::RING, "LDS budget");
 
-  // Rasterization: logical ids walk rectangles of GR row tiles x GC column tiles (the last ones of a
-  // row group or of the tile list smaller), row tiles fastest. The blocks an XCD runs at one time are
+  // Rasterization: logical ids walk rectangles of GR row tiles x GC column tiles (for gate_up,
+  // MOE_HOT_ALIGN rows in the hot region at the list's start), row tiles fastest. The blocks an XCD runs at one time are
   // consecutive logical ids, so they cover about one rectangle and read GR A slices and GC B slices
   // per K step between them instead of one of each per block.
   constexpr int GR = GATE_UP ? MOE_PF_GROUP_ROWS_GU : MOE_PF_GROUP_ROWS_DN;
   constexpr int GC = GATE_UP ? MOE_PF_GROUP_COLS_GU : MOE_PF_GROUP_COLS_DN;
-  const int64_t sg = L / ((int64_t)GR * ncol_max), within = L % ((int64_t)GR * ncol_max);
-  const int64_t gr = min((int64_t)GR, n_tiles - sg * GR);
-  const int64_t cg = within / (gr * GC), w2 = within % (gr * GC);
-  const int64_t tile_id = sg * GR + w2 % gr;
-  const int ct = (int)(cg * GC + w2 / gr);
+  int64_t tile_id;
+  int ct;
+#ifndef MOE_HOT_DOWN
+#define MOE_HOT_DOWN 0  // 1: the down GEMM walks the hot region in MOE_HOT_ALIGN-row rectangles too
+#endif
+  if ((GATE_UP || MOE_HOT_DOWN) && L < n_hot * ncol_max) {
+    raster<MOE_HOT_ALIGN, GC>(L, ncol_max, n_hot, tile_id, ct);
+  } else if (GATE_UP || MOE_HOT_DOWN) {
+    raster<GR, GC>(L - n_hot * ncol_max, ncol_max, n_tiles - n_hot, tile_id, ct);
+    tile_id += n_hot;
+  } else {
+    raster<GR, GC>(L, ncol_max, n_tiles, tile_id, ct);  // the hot region is a multiple of GR rows
+  }
   const Tile tile = a.tiles[tile_id];
   if (tile.rows <= 0) return;  // padding
   const ExpertProblem P = pick_problem(a, tile.problem);
@@ -464,6 +485,7 @@ __global__ __launch_bounds__(512, 1) void grouped_bf16_w8(GroupedArgs a, int nco
   static_assert(8 * 64 * (Wave8Tile<GATE_UP>::OC + 8) * 2 + 256 * 4 <= RING - 4, "claim word overlaps the epilogue");
   int* claim_word = (int*)(lds + RING - 4);
   const int64_t n_tiles = *a.n_tiles, nvalid = n_tiles * ncol_max;
+  const int64_t n_hot = a.n_hot ? min((int64_t)*a.n_hot, n_tiles) : 0;
   const int64_t q = nvalid >> 3, r = nvalid & 7;
   const int x = blockIdx.x & 7;  // the XCD the hardware dealt this block to
   for (int v = 0; v < 8; ++v) {
@@ -475,7 +497,7 @@ __global__ __launch_bounds__(512, 1) void grouped_bf16_w8(GroupedArgs a, int nco
       const int64_t j = *claim_word;
       __syncthreads();  // every wave has read claim before it is overwritten
       if (j >= len) break;
-      w8_block<GATE_UP>(a, ncol_max, n_tiles, start + j, lds);
+      w8_block<GATE_UP>(a, ncol_max, n_tiles, n_hot, start + j, lds);
     }
   }
 }

@@ -95,7 +95,7 @@ Workspace layout(const moe_config* c, int64_t N) {
   w.inv_row = take(sizeof(int32_t) * N * k);
   w.tiles0 = take(sizeof(Tile) * w.max_tiles0);
   w.tiles1 = take(sizeof(Tile) * w.max_tiles1);
-  w.ntiles = take(sizeof(int32_t) * 18);  // two tile counts, 8 work counters per list
+  w.ntiles = take(sizeof(int32_t) * 20);  // two tile counts, 8 work counters per list, two hot counts
   w.H = take(es * N * k * d);
   w.Hsh = take(es * N * dsh);
   w.Y = take(es * N * k * D);
@@ -146,7 +146,7 @@ DenseWorkspace dense_layout(int64_t N, int dff, int dtype) {
   };
   w.tiles0 = take(sizeof(Tile) * w.max_tiles);
   w.tiles1 = take(sizeof(Tile) * w.max_tiles);
-  w.ntiles = take(sizeof(int32_t) * 18);  // two tile counts, 8 work counters per list
+  w.ntiles = take(sizeof(int32_t) * 20);  // two tile counts, 8 work counters per list, two hot counts
   w.H = take(es * N * dff);
   w.total = o;
   return w;
@@ -253,8 +253,10 @@ moe_status dispatch_impl(const moe_config* c, int64_t N, const int32_t* idx, int
 moe_status forward_dispatch(const moe_config* c, int64_t N, const int32_t* idx, void* ws, const Workspace& L,
                             hipStream_t s) {
   int32_t* ntiles = at<int32_t>(ws, L.ntiles);
-  const TileSpec t0{L.bm0, at<Tile>(ws, L.tiles0), ntiles, small_expert_rows(c->dtype, L.bm0), ntiles + 2};
-  const TileSpec t1{L.bm1, at<Tile>(ws, L.tiles1), ntiles + 1, small_expert_rows(c->dtype, L.bm1), ntiles + 10};
+  const TileSpec t0{L.bm0, at<Tile>(ws, L.tiles0), ntiles, small_expert_rows(c->dtype, L.bm0), ntiles + 2,
+                    ntiles + 18};
+  const TileSpec t1{L.bm1, at<Tile>(ws, L.tiles1), ntiles + 1, small_expert_rows(c->dtype, L.bm1), ntiles + 10,
+                    ntiles + 19};
   return dispatch_impl(c, N, idx, at<int32_t>(ws, L.counts), at<int32_t>(ws, L.offsets),
                        at<int32_t>(ws, L.sorted_pair), at<int32_t>(ws, L.inv_row), at<int32_t>(ws, L.chunk_counts),
                        at<int32_t>(ws, L.chunk_base), t0, t1, L.pick, s);
@@ -268,6 +270,7 @@ hipError_t grouped_gemm(bool gate_up, int dtype, GroupedArgs g, void* ws, const 
   g.tiles = at<Tile>(ws, list ? L.tiles1 : L.tiles0);
   g.n_tiles = block + list;
   g.work_ctr = block + ctr;
+  g.n_hot = block + 18 + list;
   g.bm = list ? L.bm1 : L.bm0;
   const int64_t max_tile_count = list ? L.max_tiles1 : L.max_tiles0;
   return gate_up ? launch_gate_up(dtype, g, max_tile_count, s) : launch_down(dtype, g, max_tile_count, s);
@@ -461,7 +464,7 @@ moe_status moe_dispatch(const moe_config* cfg, int64_t N, const int32_t* topk_id
       return MOE_ERR_HIP;
     return MOE_OK;
   }
-  const TileSpec none{0, nullptr, nullptr, 0, nullptr};
+  const TileSpec none{0, nullptr, nullptr, 0, nullptr, nullptr};
   return dispatch_impl(cfg, N, topk_idx, counts, offsets, sorted_pair, inv_row, at<int32_t>(workspace, L.chunk_counts),
                        at<int32_t>(workspace, L.chunk_base), none, none, 0, s);
 }
@@ -562,8 +565,8 @@ moe_status moe_dense_forward(int64_t N, int32_t D, int32_t dff, int32_t dtype, f
   hipStream_t s = (hipStream_t)stream;
   void* ws = workspace;
   int32_t* ntiles = at<int32_t>(ws, L.ntiles);
-  TileSpec t0{L.bm, at<Tile>(ws, L.tiles0), ntiles, 0, ntiles + 2};
-  TileSpec t1{L.bm, at<Tile>(ws, L.tiles1), ntiles + 1, 0, ntiles + 10};
+  TileSpec t0{L.bm, at<Tile>(ws, L.tiles0), ntiles, 0, ntiles + 2, nullptr};
+  TileSpec t1{L.bm, at<Tile>(ws, L.tiles1), ntiles + 1, 0, ntiles + 10, nullptr};
   if (launch_dense_tiles(N, t0, t1, s) != hipSuccess) return MOE_ERR_HIP;
   // one dense problem through the grouped GEMMs: no gather, no row scale
   GroupedArgs g{};

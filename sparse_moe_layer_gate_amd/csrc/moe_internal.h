@@ -81,6 +81,18 @@ constexpr int kDispatchChunk = 256;  // tokens per dispatch block
 #ifndef MOE_TILE_ALIGN
 #define MOE_TILE_ALIGN 2
 #endif
+// Experts with at least MOE_HOT_TILES tiles ("hot") go first in the 256-row lists, padded to a multiple
+// of MOE_HOT_ALIGN slots, and the prefill gate_up kernel walks that region in MOE_HOT_ALIGN-row
+// rectangles, so that four row tiles of a hot expert share each of its weight panels in L2 (0: no hot
+// region). Same box, layer ms (mean of two runs): skewed GLM-4.5 4.01 -> 3.96, mild-skew GLM-4.5
+// 3.84 -> 3.80, GLM-5, Air and the 288-expert prefill unchanged; the same rectangles in the down GEMM
+// as well were no better, and a threshold of 5 tiles was between the two.
+#ifndef MOE_HOT_TILES
+#define MOE_HOT_TILES 3
+#endif
+#ifndef MOE_HOT_ALIGN
+#define MOE_HOT_ALIGN 4
+#endif
 
 // ---- router ----
 struct RouterPlan {
@@ -107,6 +119,7 @@ struct TileSpec {
   int small_max;     // > 0: tiles of experts with 1..small_max rows go after all the others, and
                      // the other experts' tiles are padded to MOE_TILE_ALIGN slots
   int32_t* work_ctr;  // the list's 8 work counters (persistent kernels), zeroed with the list; or nullptr
+  int32_t* n_hot;     // output: slots of the hot region at the list's start (or nullptr)
 };
 hipError_t launch_count(const int32_t* idx, int64_t N, int k, int E, int32_t* chunk_counts, hipStream_t s);
 hipError_t launch_scan(const int32_t* chunk_counts, int nchunks, int64_t N, int k, int E, int n_shared_problem,
@@ -146,6 +159,7 @@ struct GroupedArgs {
   float swiglu_limit;      // gate_up epilogue clamp bound (0: plain SwiGLU)
   int64_t gather_rows;     // rows of the matrix that gathered A rows index (x); 0 when unknown
   int32_t* work_ctr;       // 8 counters, zero at launch: per-XCD work claims of the persistent kernels
+  const int32_t* n_hot;    // slots of the list's hot region (MOE_HOT_TILES), or nullptr: none
 };
 // Field-wise select keeps a problem descriptor in scalar registers (a dynamically indexed
 // kernel-argument array would be copied to scratch).
