@@ -58,10 +58,11 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 //    and the matching 64 up rows, so SwiGLU pairs stay in one wave);
 //  - the waves of half g load rows [128 g, 128 g + 128) of both operands, four direct loads per lane
 //    of each per step (buffer_load_dwordx4 ... lds through raw buffer descriptors);
-//  - per K step t a wave issues its A loads of step t + 1, reads the fragments of the step's first 32
-//    K values, reads the second half's fragments while the first half's MFMAs run, issues its B loads
-//    of step t + 2, runs the second half's MFMAs, waits for its loads of step t + 1 and meets the
-//    others at a barrier. A stage is refilled only after every wave has passed the barrier that
+//  - per K step t a wave issues its A loads of step t + 1 and works through the step's four 16-wide K
+//    slices with the fragments double-buffered by slice: the reads of slice s + 1 are in flight while
+//    slice s's MFMAs run. It issues its B loads of step t + 2 with the second slice, waits for its
+//    loads of step t + 1, meets the others at a barrier, and then reads step t + 1's first slice while
+//    the last slice's MFMAs run. A stage is refilled only after every wave has passed the barrier that
 //    follows its last read; A loads get about one step to land and B loads two.
 template <bool GATE_UP>
 struct Wave8Tile {
@@ -125,8 +126,6 @@ __device__ __attribute__((always_inline)) inline void wave8_loop(char* lds, __am
   int b_off[TN];
 #pragma unroll
   for (int j = 0; j < TN; ++j) b_off[j] = (T::b_row(j, wn) + (lane & 31)) * ROWB;
-  // fragments of the lo and hi K halves in separate registers
-  bf16x8 af[2][2][MI > 0 ? MI : 1], bfr[2][2][TN];
   const int half_off = grp * (T::OPB / 2) + q * 1024;  // this wave's first LDS chunk run in a stage
 
   // this wave's loads of step kstep: load i fills chunks [(4 i + q) 64, + 64) of its half's rows; the K
@@ -146,30 +145,34 @@ __device__ __attribute__((always_inline)) inline void wave8_loop(char* lds, __am
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrcB, (lds_void*)(dst + i * 4096), 16, (int)offB[i], kstep * T::BK * 2,
                                                0, 0);
   };
-  // operand fragments of K slices 2h, 2h + 1 of step kstep (issued only; wait_lgkm0 waits for them)
-  auto read_frags = [&](int kstep, int h) {
+  // Fragments of one 16-wide K slice (kstep's slice sl) into buffer buf; the reads are only issued
+  // here, and the waits below order them. A wave with no valid rows reads nothing.
+  constexpr int NR = MI > 0 ? MI + TN : 0;  // LDS reads per slice
+  bf16x8 af[2][MI > 0 ? MI : 1], bfr[2][TN];
+  auto read_slice = [&](int kstep, int sl, int buf) {
+    if (MI == 0) return;
     const char* sa = lds + (kstep % T::A_STAGES) * T::OPB;
     const char* sb = lds + T::B_BASE + (kstep % T::B_STAGES) * T::OPB;
+    const int coff = ((2 * sl + (lane >> 5)) ^ sw) * 16;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int coff = ((2 * (2 * h + s) + (lane >> 5)) ^ sw) * 16;
+    for (int j = 0; j < TN; ++j) bfr[buf][j] = *(const bf16x8*)(sb + b_off[j] + coff);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) bfr[h][s][j] = *(const bf16x8*)(sb + b_off[j] + coff);
-#pragma unroll
-      for (int i = 0; i < MI; ++i) af[h][s][i] = *(const bf16x8*)(sa + a_off + i * 32 * ROWB + coff);
-    }
+    for (int i = 0; i < MI; ++i) af[buf][i] = *(const bf16x8*)(sa + a_off + i * 32 * ROWB + coff);
   };
-  auto compute = [&](int h) {
+  auto compute = [&](int buf) {
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[h][s][i], bfr[h][s][j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf][i], bfr[buf][j], acc[i][j], 0, 0, 0);
   };
+  // Scheduling fence: without it the compiler sinks each fragment read next to its first MFMA and
+  // waits for it there, so the matrix core idles for an LDS round trip per read.
+  auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+  // s_waitcnt lgkmcnt(NR): all but the newest slice's reads have landed
+  auto wait_older_slices = [] { __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (NR << 8)); };
 
-  // prologue: this wave's rows of A(0), B(0), B(1); wait for step 0
+  // prologue: this wave's rows of A(0), B(0), B(1); wait for step 0; read its first slice
   issue_a(0);
   issue_b(0);
   if (nk > 1) {
@@ -179,32 +182,51 @@ __device__ __attribute__((always_inline)) inline void wave8_loop(char* lds, __am
     wait_vmcnt<0>();
   }
   bare_barrier();
+  read_slice(0, 0, 0);
+  fence();
   // The steps that issue both operands' loads run in a loop of their own, free of the branches and of
   // the variable waits of the last two steps, which are peeled (with the small-tile loop peeled the same
   // way, against one loop with the conditions inside: dense FFN gate_up 1.74 -> 1.65 ms, skewed GLM-4.5
-  // layer 4.22 -> 4.08 ms, Air 1.75 -> 1.63 ms; 239 -> 207 VGPRs in gate_up).
-  auto step = [&](int kt, auto more_a, auto more_b) {
-    constexpr bool MA = decltype(more_a)::value, MB = decltype(more_b)::value;
-    // step kt is in LDS: A stage kt % 2, B stage kt % 3
+  // layer 4.22 -> 4.08 ms, Air 1.75 -> 1.63 ms; 239 -> 207 VGPRs in gate_up). The slice double buffer
+  // against reading whole K halves, which the compiler had interleaved read by read with the MFMAs:
+  // gate_up 1-2% faster on every layer (skewed GLM-4.5 2.35 -> 2.34 ms, mild skew 2.23 -> 2.19,
+  // GLM-5 3.88 -> 3.83, Air 0.90 -> 0.89).
+  auto step = [&](int kt, auto more_a, auto more_b, auto last) {
+    constexpr bool MA = decltype(more_a)::value, MB = decltype(more_b)::value, LAST = decltype(last)::value;
+    // step kt is in LDS (A stage kt % 2, B stage kt % 3), its slice 0 being read into buffer 0
     if (MA) issue_a(kt + 1);  // into the A stage step kt - 1 used (every wave is done with it)
-    read_frags(kt, 0);
-    wait_lgkm0();
-    read_frags(kt, 1);        // lands while the lo half's MFMAs run
+    read_slice(kt, 1, 1);
+    fence();
+    wait_older_slices();
     compute(0);
+    fence();
+    read_slice(kt, 2, 0);
+    fence();
+    wait_older_slices();
     if (MB) issue_b(kt + 2);  // into the B stage step kt - 1 used
-    wait_lgkm0();
     compute(1);
+    fence();
+    read_slice(kt, 3, 1);
+    fence();
+    wait_older_slices();
+    compute(0);
+    fence();
+    wait_lgkm0();
     // step kt + 1 has landed (only this wave's B loads of step kt + 2 may still be in flight)
     if (MB)
       wait_vmcnt<NL>();
     else if (MA)
       wait_vmcnt<0>();
     bare_barrier();
+    if (!LAST) read_slice(kt + 1, 0, 0);
+    fence();
+    compute(1);  // the last slice, while the next step's first reads land
+    fence();
   };
   int kt = 0;
-  for (; kt + 2 < nk; ++kt) step(kt, BoolC<true>{}, BoolC<true>{});
-  if (kt + 1 < nk) step(kt++, BoolC<true>{}, BoolC<false>{});
-  step(kt, BoolC<false>{}, BoolC<false>{});
+  for (; kt + 2 < nk; ++kt) step(kt, BoolC<true>{}, BoolC<true>{}, BoolC<false>{});
+  if (kt + 1 < nk) step(kt++, BoolC<true>{}, BoolC<false>{}, BoolC<false>{});
+  step(kt, BoolC<false>{}, BoolC<false>{}, BoolC<true>{});
 }
 
 // The K loop of one wave for a tile of at most 64 valid rows. Such a block is a stream of its expert's
@@ -213,6 +235,13 @@ __device__ __attribute__((always_inline)) inline void wave8_loop(char* lds, __am
 // loads in flight where the large-tile ring has two. Every wave issues one A load (its 8 of the 64
 // rows; rows past the tile repeat its last row) and NL B loads per step, so a fixed count of loads
 // per step orders the ring through vmcnt. Waves 0-3 compute 32 rows each (m0 = 0 or 32, MI <= 1).
+// Cache policy of the small-tile ring's weight loads: non-temporal (the NT bit, 2 on gfx950). A small
+// tile is its expert's only tile, so each of these weight bytes is read once per launch, and the hint
+// keeps that stream from evicting the hot experts' weight panels, which several row tiles share in L2:
+// skewed GLM-4.5 gate_up 2.35 -> 2.29 ms (124 experts of at most 64 rows, 3.9 GB of their weights),
+// the other layers within 1%. (On every B load it costs 1-12%: there the panels are reused.)
+constexpr int kStreamPolicy = 2;
+
 template <bool GATE_UP>
 struct SmallRing {
   static constexpr int S = 4;                                  // stages of A and of B
@@ -248,7 +277,7 @@ __device__ __attribute__((always_inline)) inline void wave8_loop_small(char* lds
 #pragma unroll
     for (int i = 0; i < NL; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrcB, (lds_void*)(db + i * 4096), 16, (int)offB[i], kstep * T::BK * 2,
-                                               0, 0);
+                                               0, kStreamPolicy);
   };
   auto read_frags = [&](int kstep, int h) {
     const char* sa = lds + (kstep % S) * R::A_STAGE;
