@@ -391,10 +391,11 @@ __device__ __forceinline__ void w8_block(const GroupedArgs& a, int ncol_max, int
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int grp = wave >> 2, q = wave & 3;
-  // gate_up tiles of at most 64 rows run the weight-streaming ring (wave8_loop_small): waves 0-3
-  // compute 32 rows each; otherwise each wave computes 64 of the 256 rows. (The down GEMM's short K
-  // loop did not gain from it: 1.37 -> 1.41 ms on the skewed GLM-4.5 layer.)
-  const bool small = GATE_UP && tile.rows <= 64;
+  // Tiles of at most 64 rows run the weight-streaming ring (wave8_loop_small): waves 0-3 compute 32
+  // rows each; otherwise each wave computes 64 of the 256 rows. (The down GEMM, 24 K steps, gains only
+  // with the ring's non-temporal weight loads: skewed GLM-4.5 down 1.36 -> 1.33 ms, 1.37 -> 1.41 ms
+  // without the hint; the other layers within 0.5%.)
+  const bool small = tile.rows <= 64;
   const int m0 = small && grp == 0 ? (q & 1) * 32 : grp * 128 + (q & 1) * 64, wn = q >> 1;
 
   // Direct-load sources: chunk p of this half's 128 rows is row 128 g + p / 8, slot p % 8, which holds
