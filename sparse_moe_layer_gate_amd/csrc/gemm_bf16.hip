@@ -235,9 +235,10 @@ __device__ __attribute__((always_inline)) inline void wave8_loop(char* lds, __am
 // loads in flight where the large-tile ring has two. Every wave issues one A load (its 8 of the 64
 // rows; rows past the tile repeat its last row) and NL B loads per step, so a fixed count of loads
 // per step orders the ring through vmcnt. Waves 0-3 compute 32 rows each (m0 = 0 or 32, MI <= 1).
-// Cache policy of the small-tile ring's weight loads: non-temporal (the NT bit, 2 on gfx950). A small
-// tile is its expert's only tile, so each of these weight bytes is read once per launch, and the hint
-// keeps that stream from evicting the hot experts' weight panels, which several row tiles share in L2:
+// Cache policy of the small-tile ring's weight loads: non-temporal (the NT bit, 2 on gfx950). Almost
+// every small tile is its expert's only tile (the rest are the last tiles of larger experts), so these
+// weight bytes are read once per launch, and the hint keeps that stream from evicting the hot experts'
+// weight panels, which several row tiles share in L2:
 // skewed GLM-4.5 gate_up 2.35 -> 2.29 ms (124 experts of at most 64 rows, 3.9 GB of their weights),
 // the other layers within 1%. (On every B load it costs 1-12%: there the panels are reused.)
 constexpr int kStreamPolicy = 2;
