@@ -46,9 +46,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // ---- eight-wave kernel for 256-row tiles ----
 //
 // With one wave per SIMD, the wave that issues a K step's direct loads stalls while the texture path
-// accepts them (measured: a CU takes 1 KiB global_load_lds_dwordx4 instructions at ~26-30 bytes per
-// clock, so the 64 KiB of operands of a 256 x 256 x 64 step hold a wave about as long as the step's
-// MFMAs run), and its SIMD's matrix core idles meanwhile. Here each SIMD runs two waves (w and w + 4),
+// accepts them (the CU's waves issue theirs within a short window of the step, so they queue behind
+// one another), and its SIMD's matrix core idles meanwhile. Here each SIMD runs two waves (w and w + 4),
 // each with its own 64 x 128 share of the tile, its own fragment reads and an eighth of every step's
 // loads: while one of them waits on the load path, the other keeps the matrix core busy.
 //  - block tile 256 x 256, BK = 64 (whole 128-byte lines per row and load); A in a two-stage ring, B
